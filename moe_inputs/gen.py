@@ -129,12 +129,15 @@ def _uniform_bytes(rng: np.random.Generator, shape) -> np.ndarray:
 def make_layer_inputs(T: int, E: int, k: int, seed: int = 0,
                       zipf_s: Optional[float] = None,
                       H: int = H_DEFAULT, I: int = I_DEFAULT,
-                      scale_exp_range=(-8, -5)) -> Dict[str, np.ndarray]:
+                      scale_exp_range=(-8, -5),
+                      router_only: bool = False) -> Dict[str, np.ndarray]:
     """Draw one input set of the layer. Returns host arrays:
 
     x [T,H] u16 (bf16 bits), Wr [E,H] f32, br [E] f32,
     w13_codes [E,2I,H/2] u8, w13_scales [E,2I,H/32] u8, b13 [E,2I] u16,
     w2_codes [E,H,I/2] u8, w2_scales [E,H,I/32] u8, b2 [E,H] u16.
+    ``router_only`` stops after the router inputs (x, Wr, br); the draws of
+    those three are the same as in the full set.
     """
     if H % 32 or I % 32:
         raise ValueError("H and I must be multiples of the 32-element MX block")
@@ -143,20 +146,22 @@ def make_layer_inputs(T: int, E: int, k: int, seed: int = 0,
     x = bf16_bits_from_f32(rng.standard_normal((T, H), dtype=np.float32))
     Wr = (rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.02))
     br = (rng.standard_normal(E, dtype=np.float32) * np.float32(0.02))
+    if zipf_s is not None:
+        zrng = np.random.Generator(np.random.PCG64([seed, 0x5A1F]))
+        norms = np.sqrt((Wr.astype(np.float64) ** 2).sum(axis=1))
+        br = _fit_zipf_bias(norms, k, zipf_s, zrng)
+    if router_only:
+        return dict(x=x, Wr=Wr, br=br)
     w13_codes = _uniform_bytes(rng, (E, 2 * I, H // 2))
     w13_scales = (127 + rng.integers(lo, hi + 1, size=(E, 2 * I, H // 32))).astype(np.uint8)
     b13 = bf16_bits_from_f32(rng.standard_normal((E, 2 * I), dtype=np.float32) * np.float32(0.02))
     w2_codes = _uniform_bytes(rng, (E, H, I // 2))
     w2_scales = (127 + rng.integers(lo, hi + 1, size=(E, H, I // 32))).astype(np.uint8)
     b2 = bf16_bits_from_f32(rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.02))
-    if zipf_s is not None:
-        zrng = np.random.Generator(np.random.PCG64([seed, 0x5A1F]))
-        norms = np.sqrt((Wr.astype(np.float64) ** 2).sum(axis=1))
-        br = _fit_zipf_bias(norms, k, zipf_s, zrng)
     return dict(x=x, Wr=Wr, br=br, w13_codes=w13_codes, w13_scales=w13_scales,
                 b13=b13, w2_codes=w2_codes, w2_scales=w2_scales, b2=b2)
 
 
-def make_config_inputs(index: int, seed: int = 0) -> Dict[str, np.ndarray]:
+def make_config_inputs(index: int, seed: int = 0, router_only: bool = False) -> Dict[str, np.ndarray]:
     c = LAYER_CONFIGS[index]
-    return make_layer_inputs(c.T, c.E, c.k, seed=seed, zipf_s=c.zipf_s)
+    return make_layer_inputs(c.T, c.E, c.k, seed=seed, zipf_s=c.zipf_s, router_only=router_only)

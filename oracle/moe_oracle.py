@@ -143,7 +143,9 @@ def swiglu(gu: np.ndarray, alpha: float = SWIGLU_ALPHA,
     """gpt-oss gated unit on interleaved gate/up columns."""
     gate = np.minimum(gu[..., 0::2], limit)
     up = np.clip(gu[..., 1::2], -limit, limit)
-    glu = gate / (1.0 + np.exp(-alpha * gate))
+    # exp overflows to inf for very negative gates; gate / inf is the correct limit 0
+    with np.errstate(over="ignore"):
+        glu = gate / (1.0 + np.exp(-alpha * gate))
     return (up + 1.0) * glu
 
 

@@ -1,0 +1,60 @@
+"""ctypes loader of libmoe_mi355x.so and the prototypes of include/moe.h.
+
+Loading fails loudly when the library has not been built: there is no other
+implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmoe_mi355x.so")
+
+# every symbol declared in include/moe.h
+EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
+            "moe_combine", "moe_forward", "moe_status_string")
+
+MOE_SUCCESS = 0
+STATUS_NAMES = {
+    0: "MOE_SUCCESS",
+    1: "MOE_ERROR_INVALID_VALUE",
+    2: "MOE_ERROR_MISALIGNED",
+    3: "MOE_ERROR_WORKSPACE",
+    4: "MOE_ERROR_UNSUPPORTED",
+    5: "MOE_ERROR_HIP",
+}
+
+_lib = None
+
+
+class MoeLibraryMissing(ImportError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MoeLibraryMissing(
+            f"{LIB_PATH} is missing: build it first (python -m sparse_moe_ffn_fp32_amd.build "
+            "or __graft_entry__.build()); the MoE layer has no non-HIP implementation")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, SZ, ST = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int
+    L.moe_workspace_size.argtypes = [I, I, I]
+    L.moe_workspace_size.restype = SZ
+    L.moe_status_string.argtypes = [ST]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_route.argtypes = [P, P, P, I, I, I, P, P, P, P]
+    L.moe_route.restype = ST
+    L.moe_permute.argtypes = [P, I, I, I, P, P, P, P, SZ, P]
+    L.moe_permute.restype = ST
+    L.moe_expert_ffn.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, P, SZ, P]
+    L.moe_expert_ffn.restype = ST
+    L.moe_combine.argtypes = [P, P, I, I, P, P]
+    L.moe_combine.restype = ST
+    L.moe_forward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, P, SZ, P]
+    L.moe_forward.restype = ST
+    _lib = L
+    return L

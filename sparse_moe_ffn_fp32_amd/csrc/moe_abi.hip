@@ -1,0 +1,238 @@
+// C ABI of the MoE layer: argument validation on the host, workspace carve-up,
+// kernel launches on the caller's stream. No allocation, no host sync (unless
+// MOE_DEBUG_SYNC=1 is set in the environment, which synchronises and checks
+// after every launch).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "moe.h"
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace {
+
+using moe::FfnArgs;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+  size_t ids, w, counts, offsets, sorted, h, total;
+};
+
+bool sizes_ok(int T, int E, int k) {
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < k || E > MOE_MAX_EXPERTS) return false;
+  return (long long)T * k <= MOE_MAX_ROUTED;
+}
+
+WsLayout layout(int T, int E, int k) {
+  const size_t n = (size_t)T * k;
+  WsLayout l;
+  size_t off = 0;
+  l.ids = off;      off = align_up(off + n * 4);
+  l.w = off;        off = align_up(off + n * 4);
+  l.counts = off;   off = align_up(off + (size_t)E * 4);
+  l.offsets = off;  off = align_up(off + (size_t)(E + 1) * 4);
+  l.sorted = off;   off = align_up(off + n * 4);
+  l.h = off;        off = align_up(off + n * (size_t)moe::kI * 2);
+  l.total = off;
+  return l;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Current device must be gfx950; the answer is cached per device.
+std::atomic<int> g_arch_state[64];  // 0 unknown, 1 gfx950, 2 other
+
+moe_status_t check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERROR_HIP;
+  if (dev < 0 || dev >= 64) return MOE_ERROR_UNSUPPORTED;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERROR_HIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? MOE_SUCCESS : MOE_ERROR_UNSUPPORTED;
+}
+
+bool debug_sync() {
+  static const int on = [] {
+    const char* v = std::getenv("MOE_DEBUG_SYNC");
+    return (v && v[0] == '1') ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+moe_status_t after_launch(hipError_t err, hipStream_t s) {
+  if (err != hipSuccess) return MOE_ERROR_HIP;
+  if (debug_sync()) {
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERROR_HIP;
+    if (hipGetLastError() != hipSuccess) return MOE_ERROR_HIP;
+  }
+  return MOE_SUCCESS;
+}
+
+#define MOE_TRY(expr)                       \
+  do {                                      \
+    moe_status_t st_ = (expr);              \
+    if (st_ != MOE_SUCCESS) return st_;     \
+  } while (0)
+
+moe_status_t check_weights(const uint8_t* w13c, const uint8_t* w13s, const uint16_t* b13,
+                           const uint8_t* w2c, const uint8_t* w2s, const uint16_t* b2) {
+  if (!w13c || !w13s || !b13 || !w2c || !w2s || !b2) return MOE_ERROR_INVALID_VALUE;
+  if (!aligned(w13c, 16) || !aligned(w2c, 16) || !aligned(b13, 2) || !aligned(b2, 2))
+    return MOE_ERROR_MISALIGNED;
+  return MOE_SUCCESS;
+}
+
+moe_status_t check_ws(void* ws, size_t ws_bytes, int T, int E, int k) {
+  if (!ws || !aligned(ws, kAlign)) return MOE_ERROR_WORKSPACE;
+  if (ws_bytes < layout(T, E, k).total) return MOE_ERROR_WORKSPACE;
+  return MOE_SUCCESS;
+}
+
+FfnArgs ffn_args(const uint16_t* act, const int32_t* offsets, const int32_t* sorted_rows,
+                 const uint8_t* codes, const uint8_t* scales, const uint16_t* bias, int N, int E,
+                 int k, int gather) {
+  FfnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.act = act;
+  a.offsets = offsets;
+  a.sorted_rows = sorted_rows;
+  a.codes = codes;
+  a.scales = scales;
+  a.bias = bias;
+  a.N = N;
+  a.E = E;
+  a.k = k;
+  a.gather = gather;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(int T, int E, int k) {
+  if (!sizes_ok(T, E, k)) return 0;
+  return layout(T, E, k).total;
+}
+
+const char* moe_status_string(moe_status_t status) {
+  switch (status) {
+    case MOE_SUCCESS: return "MOE_SUCCESS";
+    case MOE_ERROR_INVALID_VALUE: return "MOE_ERROR_INVALID_VALUE: null pointer or size out of range";
+    case MOE_ERROR_MISALIGNED: return "MOE_ERROR_MISALIGNED: pointer lacks the required alignment";
+    case MOE_ERROR_WORKSPACE: return "MOE_ERROR_WORKSPACE: workspace missing, misaligned or too small";
+    case MOE_ERROR_UNSUPPORTED: return "MOE_ERROR_UNSUPPORTED: current device is not gfx950";
+    case MOE_ERROR_HIP: return "MOE_ERROR_HIP: a HIP runtime call or kernel launch failed";
+  }
+  return "unknown moe_status_t";
+}
+
+moe_status_t moe_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
+                       int32_t* topk_ids, float* topk_w, float* logits, void* stream) {
+  if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !Wr || !br || !topk_ids || !topk_w) return MOE_ERROR_INVALID_VALUE;
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(br, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4) || !aligned(logits, 4))
+    return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(moe::launch_route(x, Wr, br, T, E, k, topk_ids, topk_w, logits, nullptr, s), s);
+}
+
+moe_status_t moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* counts,
+                         int32_t* offsets, int32_t* sorted_rows, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!topk_ids || !counts || !offsets || !sorted_rows) return MOE_ERROR_INVALID_VALUE;
+  if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_rows, 4))
+    return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(moe::launch_permute(topk_ids, T * k, E, counts, offsets, sorted_rows, s), s);
+}
+
+moe_status_t moe_expert_ffn(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_rows,
+                            const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
+                            const uint8_t* w2_codes, const uint8_t* w2_scales, const uint16_t* b2,
+                            int T, int E, int k, float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !offsets || !sorted_rows || !y) return MOE_ERROR_INVALID_VALUE;
+  MOE_TRY(check_weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2));
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(offsets, 4) || !aligned(sorted_rows, 4))
+    return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const WsLayout l = layout(T, E, k);
+  uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + l.h);
+  const int n = T * k;
+  FfnArgs a13 = ffn_args(x, offsets, sorted_rows, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
+  a13.h_out = h;
+  MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));
+  FfnArgs a2 = ffn_args(h, offsets, sorted_rows, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
+  a2.y_out = y;
+  return after_launch(moe::launch_ffn(a2, moe::EPI_STORE_Y, n, s), s);
+}
+
+moe_status_t moe_combine(const float* y, const float* topk_w, int T, int k, float* out,
+                         void* stream) {
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || (long long)T * k > MOE_MAX_ROUTED)
+    return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!y || !topk_w || !out) return MOE_ERROR_INVALID_VALUE;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_w, 4)) return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(moe::launch_combine(y, topk_w, T, k, out, s), s);
+}
+
+moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
+                         const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
+                         const uint8_t* w2_codes, const uint8_t* w2_scales, const uint16_t* b2,
+                         int T, int E, int k, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !Wr || !br || !out) return MOE_ERROR_INVALID_VALUE;
+  MOE_TRY(check_weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2));
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(out, 16) || !aligned(br, 4))
+    return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const WsLayout l = layout(T, E, k);
+  char* base = static_cast<char*>(ws);
+  int32_t* ids = reinterpret_cast<int32_t*>(base + l.ids);
+  float* w = reinterpret_cast<float*>(base + l.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + l.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + l.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + l.sorted);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + l.h);
+  const int n = T * k;
+  // router + top-k + softmax; also clears `out` for the accumulating epilogue
+  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, out, s), s));
+  MOE_TRY(after_launch(moe::launch_permute(ids, n, E, counts, offsets, sorted, s), s));
+  FfnArgs a13 = ffn_args(x, offsets, sorted, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
+  a13.h_out = h;
+  MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));
+  FfnArgs a2 = ffn_args(h, offsets, sorted, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
+  a2.topk_w = w;
+  a2.out = out;
+  return after_launch(moe::launch_ffn(a2, moe::EPI_COMBINE, n, s), s);
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Device-side building blocks shared by the MoE kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kH = 2880;            // hidden_size (GPT-OSS raw config.json fields)
+constexpr int kI = 2880;            // intermediate_size
+constexpr int kN13 = 2 * kI;        // gate/up rows, interleaved gate 2i / up 2i+1
+constexpr int kKB = kH / 32;        // MX blocks along K; H == I so both GEMMs have 90
+constexpr int kRowCodeBytes = kH / 2;   // 1440 code bytes per weight row
+constexpr int kRowScaleBytes = kKB;     // 90 scale bytes per weight row
+constexpr float kSwigluAlpha = 1.702f;  // reading: the techniques map names alpha, no value
+constexpr float kSwigluLimit = 7.0f;    // swiglu_limit, raw config.json fields
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 8;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E8M0 byte -> the fp32 scale 2^(s-127) (s in [1, 254]).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s << 23);
+}
+
+// Eight FP4 E2M1 codes (one dword, low nibble first) -> eight bf16 values
+// scaled by `scale`, in K order. v_cvt_scalef32_pk_bf16_fp4 converts the two
+// codes of one byte; the byte is chosen by the last operand.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 u4_as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// gpt-oss gated unit for one (gate, up) pair, after the bias.
+__device__ __forceinline__ float swiglu_pair(float gate, float up) {
+  gate = fminf(gate, kSwigluLimit);
+  up = fminf(fmaxf(up, -kSwigluLimit), kSwigluLimit);
+  float glu = gate / (1.0f + __expf(-kSwigluAlpha * gate));
+  return (up + 1.0f) * glu;
+}
+
+// Locate token tile `tile` of a grouped GEMM whose experts own the row ranges
+// [offsets[e], offsets[e+1]) split into tiles of `bt` rows. Run by one full
+// wave (all 64 lanes get the same answer). Returns false past the last tile.
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bt,
+                                          int tile, int& expert, int& row_begin, int& row_end) {
+  const int lane = threadIdx.x & 63;
+  int cnt[4], tiles[4];
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int e = lane * 4 + q;
+    int c = 0;
+    if (e < E) c = offsets[e + 1] - offsets[e];
+    cnt[q] = c;
+    tiles[q] = (c + bt - 1) / bt;
+    local += tiles[q];
+  }
+  // inclusive scan of per-lane totals across the wave
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  const int excl = incl - local;
+  const int total = __shfl(incl, 63, 64);
+  if (tile >= total) return false;
+  // the lane whose range holds `tile`
+  const bool mine = (tile >= excl) && (tile < incl);
+  const unsigned long long ball = __ballot(mine);
+  const int owner = __ffsll((long long)ball) - 1;
+  int e_found = 0, t_in = 0;
+  if (mine) {
+    int t = tile - excl;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (t >= 0 && t < tiles[q]) { e_found = lane * 4 + q; t_in = t; }
+      t -= tiles[q];
+    }
+  }
+  e_found = __shfl(e_found, owner, 64);
+  t_in = __shfl(t_in, owner, 64);
+  expert = e_found;
+  const int base = offsets[e_found];
+  const int n = offsets[e_found + 1] - base;
+  row_begin = base + t_in * bt;
+  row_end = base + min(n, (t_in + 1) * bt);
+  (void)cnt;
+  return true;
+}
+
+}  // namespace moe

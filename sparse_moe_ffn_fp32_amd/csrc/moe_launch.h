@@ -1,0 +1,44 @@
+// Host-side launchers of the MoE kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Epilogue : int {
+  EPI_SWIGLU = 0,   // gate/up GEMM: + b13, clamp, SwiGLU, write h (bf16, sorted order)
+  EPI_COMBINE = 1,  // down GEMM: + b2, times routing weight, atomic add into out[t]
+  EPI_STORE_Y = 2,  // down GEMM: + b2, write y[t*k + j] (fp32)
+};
+
+struct FfnArgs {
+  const uint16_t* act;          // activations, bf16 [rows, 2880]
+  const int32_t* offsets;       // [E + 1]
+  const int32_t* sorted_rows;   // [T*k]
+  const uint8_t* codes;         // [E, N, 1440]
+  const uint8_t* scales;        // [E, N, 90]
+  const uint16_t* bias;         // [E, N] bf16
+  const float* topk_w;          // [T*k]       (EPI_COMBINE)
+  uint16_t* h_out;              // [T*k, 2880] (EPI_SWIGLU)
+  float* y_out;                 // [T*k, 2880] (EPI_STORE_Y)
+  float* out;                   // [T, 2880]   (EPI_COMBINE)
+  int N;                        // weight rows: 5760 (gate/up) or 2880 (down)
+  int E;
+  int k;
+  int gather;                   // 1: activation row = sorted_rows[p] / k, 0: row p
+};
+
+hipError_t launch_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
+                        int32_t* ids, float* w, float* logits, float* zero_out, hipStream_t s);
+
+hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_rows, hipStream_t s);
+
+// Picks the weight-streaming (few rows per expert) or the tiled (many rows)
+// grouped GEMM from the mean rows per expert, n_rows / E.
+hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const float* w, int T, int k, float* out, hipStream_t s);
+
+}  // namespace moe

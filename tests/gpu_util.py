@@ -1,0 +1,70 @@
+"""Shared helpers of the GPU parity tests: host -> device transfer, the
+spec comparison metrics, and the near-tie rule for routing."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+# Pass criteria of the layer output (max error relative to the reference RMS,
+# and mean over tokens of the per-token relative L2 error).
+MAX_ERR_OVER_RMS = 2e-2
+MEAN_REL_L2 = 5e-3
+# Tokens whose k-th / (k+1)-th oracle logit gap is below this may pick a
+# different expert set.
+NEAR_TIE_GAP = 1e-4
+
+
+def to_device(inp, device="cuda"):
+    d = {}
+    for key, a in inp.items():
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        d[key] = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return d
+
+
+def weights_args(d):
+    return (d["w13_codes"], d["w13_scales"], d["b13"], d["w2_codes"], d["w2_scales"], d["b2"])
+
+
+def out_metrics(got: np.ndarray, ref: np.ndarray):
+    got = np.asarray(got, dtype=np.float64).reshape(ref.shape[0], -1)
+    ref = np.asarray(ref, dtype=np.float64).reshape(ref.shape[0], -1)
+    err = got - ref
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    max_rel = float(np.max(np.abs(err)) / rms) if rms > 0 else float(np.max(np.abs(err)))
+    nt = np.linalg.norm(ref, axis=1)
+    per_tok = np.linalg.norm(err, axis=1) / np.where(nt > 0, nt, 1.0)
+    return dict(max_err_over_rms=max_rel, mean_rel_l2=float(per_tok.mean()),
+                global_rel_l2=float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300)),
+                finite=bool(np.all(np.isfinite(got))))
+
+
+def assert_out_close(got, ref, label=""):
+    m = out_metrics(got, ref)
+    assert m["finite"], f"{label}: non-finite output"
+    assert m["max_err_over_rms"] <= MAX_ERR_OVER_RMS, (label, m)
+    assert m["mean_rel_l2"] <= MEAN_REL_L2, (label, m)
+    return m
+
+
+def check_routing(ids_gpu, w_gpu, logits64, k):
+    """Top-k sets must match the float64 oracle except on near-tie tokens.
+    Returns the GPU ids (for the oracle to follow on excluded tokens) and the
+    number of near-tie tokens whose set differed."""
+    ids_ref, gap = oracle.select_topk(logits64, k)
+    same = np.array([set(a) == set(b) for a, b in zip(ids_gpu.tolist(), ids_ref.tolist())])
+    bad = ~same & (gap >= NEAR_TIE_GAP)
+    assert not bad.any(), f"expert sets differ on {int(bad.sum())} tokens with gap >= {NEAR_TIE_GAP}"
+    # within a token: distinct experts, descending logits
+    T = ids_gpu.shape[0]
+    for t in range(T):
+        assert len(set(ids_gpu[t].tolist())) == k
+    sel = np.take_along_axis(logits64, ids_gpu.astype(np.int64), axis=1)
+    assert np.all(np.diff(sel, axis=1) <= 2e-5)
+    # weights: softmax of the float64 logits of the GPU's own set
+    w_ref = oracle.routing_weights(logits64, ids_gpu.astype(np.int64))
+    assert np.max(np.abs(w_gpu - w_ref)) < 2e-5, np.max(np.abs(w_gpu - w_ref))
+    return int((~same).sum())

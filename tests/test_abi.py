@@ -1,0 +1,144 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol declared in
+include/moe.h, and rejects bad arguments on the host before any launch.
+No compute call is made here; pointers are fake addresses the library must
+never dereference on these paths."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_ffn_fp32_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, MISALIGNED, WORKSPACE = 0, 1, 2, 3
+A = 0x10000          # a 256-byte-aligned fake device address
+P = ctypes.c_void_p
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _native.lib()
+
+
+def test_header_symbols_exported(L):
+    names = header_functions()
+    assert set(names) == set(_native.EXPORTED), names
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code, name in _native.STATUS_NAMES.items():
+        assert L.moe_status_string(code).decode().startswith(name)
+    assert b"unknown" in L.moe_status_string(99)
+
+
+def test_workspace_size(L):
+    assert L.moe_workspace_size(64, 32, 4) >= 64 * 4 * 2880 * 2
+    assert L.moe_workspace_size(0, 32, 4) > 0
+    for T, E, k in [(-1, 32, 4), (4, 32, 0), (4, 32, 9), (4, 3, 4), (4, 257, 4), (1 << 29, 32, 4)]:
+        assert L.moe_workspace_size(T, E, k) == 0, (T, E, k)
+    # the routed-slot cap: T * k <= 2^22
+    assert L.moe_workspace_size(1 << 20, 32, 4) > 0
+    assert L.moe_workspace_size((1 << 20) + 1, 32, 4) == 0
+    # grows with T and with k
+    assert L.moe_workspace_size(128, 32, 4) > L.moe_workspace_size(64, 32, 4)
+    assert L.moe_workspace_size(64, 32, 8) > L.moe_workspace_size(64, 32, 4)
+
+
+def route(L, T=4, E=32, k=4, x=A, Wr=A, br=A, ids=A, w=A, logits=None):
+    return L.moe_route(P(x), P(Wr), P(br), T, E, k, P(ids), P(w), P(logits), None)
+
+
+def test_route_validation(L):
+    assert route(L, T=0) == OK
+    assert route(L, T=-1) == INVALID
+    assert route(L, k=0) == INVALID
+    assert route(L, k=9) == INVALID
+    assert route(L, E=3) == INVALID
+    assert route(L, E=300) == INVALID
+    assert route(L, x=None) == INVALID
+    assert route(L, Wr=None) == INVALID
+    assert route(L, w=None) == INVALID
+    assert route(L, x=A + 8) == MISALIGNED
+    assert route(L, Wr=A + 4) == MISALIGNED
+    assert route(L, ids=A + 2) == MISALIGNED
+    assert route(L, logits=A + 1) == MISALIGNED
+
+
+def permute(L, T=4, E=32, k=4, ids=A, counts=A, offsets=A, rows=A, ws=A, nbytes=None):
+    if nbytes is None:
+        nbytes = L.moe_workspace_size(max(T, 0), E, k)
+    return L.moe_permute(P(ids), T, E, k, P(counts), P(offsets), P(rows), P(ws), nbytes, None)
+
+
+def test_permute_validation(L):
+    assert permute(L, T=0) == OK
+    assert permute(L, T=-3) == INVALID
+    assert permute(L, ids=None) == INVALID
+    assert permute(L, rows=None) == INVALID
+    assert permute(L, offsets=A + 2) == MISALIGNED
+    assert permute(L, ws=None) == WORKSPACE
+    assert permute(L, ws=A + 16) == WORKSPACE
+    assert permute(L, nbytes=16) == WORKSPACE
+
+
+def ffn(L, T=4, E=32, k=4, x=A, off=A, rows=A, c13=A, s13=A, b13=A, c2=A, s2=A, b2=A, y=A,
+        ws=A, nbytes=None):
+    if nbytes is None:
+        nbytes = L.moe_workspace_size(max(T, 0), E, k)
+    return L.moe_expert_ffn(P(x), P(off), P(rows), P(c13), P(s13), P(b13), P(c2), P(s2), P(b2),
+                            T, E, k, P(y), P(ws), nbytes, None)
+
+
+def test_expert_ffn_validation(L):
+    assert ffn(L, T=0) == OK
+    assert ffn(L, k=9) == INVALID
+    assert ffn(L, c13=None) == INVALID
+    assert ffn(L, b2=None) == INVALID
+    assert ffn(L, y=None) == INVALID
+    assert ffn(L, c13=A + 8) == MISALIGNED
+    assert ffn(L, c2=A + 1) == MISALIGNED
+    assert ffn(L, b13=A + 1) == MISALIGNED
+    assert ffn(L, y=A + 4) == MISALIGNED
+    assert ffn(L, x=A + 2) == MISALIGNED
+    assert ffn(L, nbytes=1024) == WORKSPACE
+
+
+def test_combine_validation(L):
+    c = lambda T=4, k=4, y=A, w=A, out=A: L.moe_combine(P(y), P(w), T, k, P(out), None)
+    assert c(T=0) == OK
+    assert c(T=-1) == INVALID
+    assert c(k=0) == INVALID
+    assert c(y=None) == INVALID
+    assert c(out=A + 4) == MISALIGNED
+    assert c(w=A + 2) == MISALIGNED
+
+
+def fwd(L, T=4, E=32, k=4, x=A, Wr=A, br=A, out=A, ws=A, nbytes=None, c13=A):
+    if nbytes is None:
+        nbytes = L.moe_workspace_size(max(T, 0), E, k)
+    return L.moe_forward(P(x), P(Wr), P(br), P(c13), P(A), P(A), P(A), P(A), P(A),
+                         T, E, k, P(out), P(ws), nbytes, None)
+
+
+def test_forward_validation(L):
+    assert fwd(L, T=0) == OK
+    assert fwd(L, T=0, x=None, out=None, ws=None) == OK   # T == 0 examines no pointer
+    assert fwd(L, T=-1) == INVALID
+    assert fwd(L, E=2) == INVALID
+    assert fwd(L, x=None) == INVALID
+    assert fwd(L, c13=None) == INVALID
+    assert fwd(L, out=A + 8) == MISALIGNED
+    assert fwd(L, Wr=A + 4) == MISALIGNED
+    assert fwd(L, ws=None) == WORKSPACE
+    assert fwd(L, nbytes=L.moe_workspace_size(4, 32, 4) - 1) == WORKSPACE

@@ -1,0 +1,266 @@
+"""HIP path vs the fp64 oracle, through the C-ABI (needs an MI355X).
+
+Routing: top-k sets bit-exact except near-tie tokens; routing weights and
+logits to fp32 accuracy. Permutation: bit-exact. Expert outputs and the layer
+output: max|err| <= 2e-2 * RMS(ref) and mean per-token relative L2 <= 5e-3.
+Small shapes run the whole oracle; the full configurations compare sampled
+tokens, and every row of the fused output against the unfused path.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_ffn_fp32_amd as moe
+from moe_inputs import LAYER_CONFIGS, make_config_inputs, make_layer_inputs
+from tests.gpu_util import (assert_out_close, check_routing, out_metrics, to_device,
+                            weights_args)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    torch.cuda.set_device(0)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def np_(t):
+    return t.cpu().numpy()
+
+
+# ---------------------------------------------------------------- library
+def test_native_library_is_loaded():
+    d = to_device(make_layer_inputs(4, 8, 2, seed=1, router_only=True))
+    moe.route(d["x"], d["Wr"], d["br"], k=2)
+    torch.cuda.synchronize()
+    maps = open("/proc/self/maps").read()
+    assert moe._native.LIB_PATH in maps
+
+
+# ---------------------------------------------------------------- route
+ROUTE_CASES = [(1, 4, 1), (2, 32, 4), (3, 32, 4), (16, 32, 4), (17, 128, 4), (64, 32, 4),
+               (100, 7, 3), (33, 256, 8), (257, 128, 4), (4096, 32, 4), (16384, 128, 4)]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_CASES)
+def test_route(T, E, k):
+    say(f"route T={T} E={E} k={k}")
+    inp = make_layer_inputs(T, E, k, seed=T * 7 + E, router_only=True)
+    d = to_device(inp)
+    ids, w, logits = moe.route(d["x"], d["Wr"], d["br"], k=k, return_logits=True)
+    torch.cuda.synchronize()
+    l64 = oracle.router_logits(inp["x"], inp["Wr"], inp["br"])
+    assert np.max(np.abs(np_(logits) - l64)) < 2e-5
+    check_routing(np_(ids), np_(w), l64, k)
+
+
+def test_route_ties_prefer_lower_index():
+    inp = make_layer_inputs(8, 16, 4, seed=2, router_only=True)
+    inp["Wr"][:] = inp["Wr"][0]
+    inp["br"][:] = 0.0
+    inp["br"][9] = 0.5
+    d = to_device(inp)
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=4)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(ids), np.tile([9, 0, 1, 2], (8, 1)))
+    assert np.allclose(np_(w)[:, 1:], np_(w)[:, 1:2])
+
+
+def test_route_deterministic():
+    inp = make_config_inputs(4, router_only=True)
+    d = to_device(inp)
+    a = moe.route(d["x"], d["Wr"], d["br"], k=4, return_logits=True)
+    b = moe.route(d["x"], d["Wr"], d["br"], k=4, return_logits=True)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# ---------------------------------------------------------------- permute
+def _random_ids(T, E, k, seed, skew=None):
+    rng = np.random.default_rng(seed)
+    p = None
+    if skew is not None:
+        p = np.arange(1, E + 1, dtype=np.float64) ** (-skew)
+        p /= p.sum()
+    ids = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        ids[t] = rng.choice(E, size=k, replace=False, p=p)
+    return ids
+
+
+PERM_CASES = [(1, 1, 1), (1, 8, 8), (16, 32, 4), (255, 32, 4), (256, 32, 4), (257, 128, 4),
+              (1000, 256, 8), (4096, 32, 4), (16384, 128, 4)]
+
+
+@pytest.mark.parametrize("T,E,k", PERM_CASES)
+def test_permute(T, E, k):
+    say(f"permute T={T} E={E} k={k}")
+    ids = _random_ids(T, E, k, seed=T + E, skew=1.3 if T >= 4096 else None)
+    counts, offsets, rows = moe.permute(torch.from_numpy(ids).cuda(), E)
+    torch.cuda.synchronize()
+    c_ref, o_ref, r_ref = oracle.expert_permutation(ids, E)
+    assert np.array_equal(np_(counts), c_ref)
+    assert np.array_equal(np_(offsets), o_ref)
+    assert np.array_equal(np_(rows), r_ref)
+
+
+# ---------------------------------------------------------------- experts
+# (T, E, k): T*k <= 24*E takes the weight-streaming kernel, above it the tiled one
+SMALL_CASES = [
+    (1, 4, 4),      # every expert selected
+    (5, 8, 2),
+    (16, 32, 4),    # the 20b T=16 shape
+    (40, 8, 4),     # experts with more than one 16-row tile
+    (130, 4, 4),    # tiled: 128-row tile + ragged tail
+    (300, 4, 1),    # tiled, k = 1
+    (256, 8, 4),
+]
+
+
+def _gpu_route_and_permute(d, E, k):
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+    counts, offsets, rows = moe.permute(ids, E)
+    return ids, w, counts, offsets, rows
+
+
+@pytest.mark.parametrize("T,E,k", SMALL_CASES)
+def test_expert_ffn_and_combine(T, E, k):
+    say(f"expert_ffn T={T} E={E} k={k}")
+    inp = make_layer_inputs(T, E, k, seed=1000 + T + E)
+    d = to_device(inp)
+    ids, w, counts, offsets, rows = _gpu_route_and_permute(d, E, k)
+    y = moe.expert_ffn(d["x"], offsets, rows, *weights_args(d), k=k)
+    out = moe.combine(y, w)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp, k, ids_override=np_(ids), keep_y=True)
+    check_routing(np_(ids), np_(w), ref["logits"], k)
+    assert_out_close(np_(y).reshape(T * k, -1), ref["y"].reshape(T * k, -1), "y")
+    assert_out_close(np_(out), ref["out"], "combine")
+
+
+@pytest.mark.parametrize("T,E,k", SMALL_CASES)
+def test_forward_small(T, E, k):
+    say(f"forward T={T} E={E} k={k}")
+    inp = make_layer_inputs(T, E, k, seed=2000 + T + E)
+    d = to_device(inp)
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+    out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=k)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp, k, ids_override=np_(ids))
+    check_routing(np_(ids), np_(w), ref["logits"], k)
+    assert_out_close(np_(out), ref["out"], "forward")
+
+
+def test_forward_one_expert_takes_all():
+    """A dominant router bias sends every token to one expert (others empty)."""
+    for T, E, k, hot in ((40, 8, 2, 5), (400, 4, 1, 2)):
+        say(f"forward hot expert T={T} E={E} k={k}")
+        inp = make_layer_inputs(T, E, k, seed=31 + T)
+        inp["br"][hot] = 50.0
+        d = to_device(inp)
+        ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+        out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=k)
+        torch.cuda.synchronize()
+        assert np.all(np_(ids)[:, 0] == hot)
+        ref = oracle.forward(inp, k, ids_override=np_(ids))
+        assert_out_close(np_(out), ref["out"], "hot expert")
+
+
+def test_forward_zero_codes_gives_weighted_down_bias():
+    T, E, k = 24, 8, 4
+    inp = make_layer_inputs(T, E, k, seed=5)
+    inp["w13_codes"][:] = 0
+    inp["w2_codes"][:] = 0
+    d = to_device(inp)
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+    out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=k)
+    torch.cuda.synchronize()
+    b2 = oracle.bf16_to_f64(inp["b2"])
+    want = np.einsum("tj,tjh->th", np_(w).astype(np.float64), b2[np_(ids)])
+    assert np.max(np.abs(np_(out) - want)) < 1e-6
+
+
+def test_forward_wide_scale_range():
+    """Scale exponents over [-20, +4] instead of [-8, -5]."""
+    T, E, k = 48, 8, 4
+    inp = make_layer_inputs(T, E, k, seed=6, scale_exp_range=(-20, 4))
+    d = to_device(inp)
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+    out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=k)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp, k, ids_override=np_(ids))
+    assert_out_close(np_(out), ref["out"], "scale range")
+
+
+def test_forward_t0_is_noop():
+    inp = make_layer_inputs(1, 8, 2, seed=7)
+    d = to_device(inp)
+    x0 = d["x"][:0]
+    out = moe.forward(x0, d["Wr"], d["br"], *weights_args(d), k=2)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 2880)
+
+
+def test_workspace_reuse_and_output_overwrite():
+    """A caller-supplied workspace full of garbage and a dirty output buffer."""
+    T, E, k = 20, 8, 4
+    inp = make_layer_inputs(T, E, k, seed=8)
+    d = to_device(inp)
+    ws = torch.full((moe.workspace_size(T, E, k),), 0xAB, dtype=torch.uint8, device="cuda")
+    out = torch.full((T, 2880), float("nan"), device="cuda")
+    a = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=k, out=out, workspace=ws)
+    b = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=k, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a).all()
+    assert torch.allclose(a, b, rtol=1e-5, atol=1e-5)
+
+
+# ---------------------------------------------------------------- full configs
+@pytest.mark.parametrize("idx", [0, 1])
+def test_forward_config_full_oracle(idx):
+    c = LAYER_CONFIGS[idx]
+    say(f"forward config {idx} ({c.name}) against the whole oracle")
+    inp = make_config_inputs(idx)
+    d = to_device(inp)
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=c.k)
+    out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=c.k)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp, c.k, ids_override=np_(ids))
+    n_tie = check_routing(np_(ids), np_(w), ref["logits"], c.k)
+    m = assert_out_close(np_(out), ref["out"], c.name)
+    say(f"  metrics {m} near-tie tokens with another set: {n_tie}")
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_forward_config_sampled(idx):
+    c = LAYER_CONFIGS[idx]
+    say(f"forward config {idx} ({c.name}): sampled tokens + fused vs unfused")
+    inp = make_config_inputs(idx)
+    d = to_device(inp)
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=c.k)
+    out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=c.k)
+    counts, offsets, rows = moe.permute(ids, c.E)
+    y = moe.expert_ffn(d["x"], offsets, rows, *weights_args(d), k=c.k)
+    out_unfused = moe.combine(y, w)
+    torch.cuda.synchronize()
+    ids_h = np_(ids)
+    logits = oracle.router_logits(inp["x"], inp["Wr"], inp["br"])
+    n_tie = check_routing(ids_h, np_(w), logits, c.k)
+    # every row: fused epilogue (atomic weighted sum) vs unfused y + combine
+    m_all = out_metrics(np_(out), np_(out_unfused).astype(np.float64))
+    assert m_all["max_err_over_rms"] < 1e-4, m_all
+    # sampled rows against the oracle (first, last and random tokens)
+    rng = np.random.default_rng(idx)
+    sample = np.unique(np.concatenate([[0, c.T - 1], rng.choice(c.T, 14, replace=False)]))
+    ref = oracle.forward(inp, c.k, tokens=sample, ids_override=ids_h)
+    m = assert_out_close(np_(out)[sample], ref["out"], c.name)
+    say(f"  sampled metrics {m}; fused vs unfused {m_all}; near-tie tokens with another set: {n_tie}")
