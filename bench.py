@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of the gpt-oss MoE FFN layer (fp32 router, MXFP4 experts) on one MI355X.
+
+A step is one moe_forward call -- router, top-k, permutation, gate/up GEMM +
+SwiGLU, down GEMM + weighted combine -- over one batch of seeded synthetic
+input already resident in HBM. Prints one JSON line on stdout.
+
+Default workload: the 20b layer at decode batch T=64 (E=32, k=4), which is
+bound by MXFP4 weight bytes. For the weight-bound shapes the step rotates over
+enough device copies of the layer's weights (>= 1 GB in total) that they
+cannot be served from the 256 MB Infinity Cache.
+
+Roofline: the dominant kernel (the gate/up GEMM) is timed with HIP events on
+the stream it runs on, in a second timed region that issues the same kernels
+through the layer's separate entry points. Its algorithmic bytes (decode) or
+FLOPs (prefill) divided by that time give `achieved`.
+
+cpu_baseline: the fp64 oracle on a bounded sample of the same workload, on
+the host cores (not a tuned CPU implementation).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec; % HBM BW (decode) / % MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+H = I = 2880
+W13_EXPERT_BYTES = 2 * I * H // 2 + 2 * I * H // 32 + 2 * I * 2   # codes + scales + bf16 bias
+W2_EXPERT_BYTES = H * I // 2 + H * I // 32 + H * 2
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["sparse_moe_ffn_fp32_amd/csrc/ffn.hip", "sparse_moe_ffn_fp32_amd/csrc/moe_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = d.get(workload)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("traffic_bytes")
+
+
+def cpu_baseline(inp, cfg, n_tokens):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    sample = np.arange(min(n_tokens, cfg.T))
+    t0 = time.perf_counter()
+    oracle.forward(inp, cfg.k, tokens=sample)
+    dt = time.perf_counter() - t0
+    return {"value": round(sample.size / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"first {sample.size} of {cfg.T} tokens: router over all {cfg.T} tokens, "
+                       f"experts for the sample, fp64 numpy, {dt:.1f} s wall")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="layer configuration index (0-4)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0,
+                    help="device copies of the weights to rotate over (0: automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens in the oracle sample (0: automatic)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the bench, run a plain device copy of this size "
+                         "(reference kernel for the HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs the layer on one GPU only: this build has no multi-GPU path "
+              "(expert-parallel sharding is a design note). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sparse_moe_ffn_fp32_amd as moe
+    from moe_inputs import LAYER_CONFIGS, make_config_inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = LAYER_CONFIGS[args.config]
+    T, E, k = cfg.T, cfg.E, cfg.k
+    log(f"bench: config {args.config} ({cfg.name}) T={T} E={E} k={k}")
+    inp = make_config_inputs(args.config, seed=args.seed)
+
+    def dev_t(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    layer_bytes = E * (W13_EXPERT_BYTES + W2_EXPERT_BYTES)
+    copies = args.copies or (max(1, math.ceil(1.0e9 / layer_bytes)) if cfg.regime == "decode" else 1)
+    x = dev_t(inp["x"])
+    sets = []
+    for _ in range(copies):
+        w = {key: dev_t(inp[key]) for key in
+             ("Wr", "br", "w13_codes", "w13_scales", "b13", "w2_codes", "w2_scales", "b2")}
+        # one-time layout conversion of the static expert weights (MXFP4 packing)
+        packed = moe.pack_expert_weights(w["w13_codes"], w["w13_scales"], w["w2_codes"], w["w2_scales"])
+        w["w13_codes"], w["w13_scales"], w["w2_codes"], w["w2_scales"] = packed
+        sets.append(w)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.workspace_size(T, E, k), dtype=torch.uint8, device=dev)
+    log(f"bench: {copies} weight copies ({copies * layer_bytes / 1e9:.2f} GB)")
+
+    def step(i):
+        w = sets[i % copies]
+        moe.forward(x, w["Wr"], w["br"], w["w13_codes"], w["w13_scales"], w["b13"],
+                    w["w2_codes"], w["w2_scales"], w["b2"], k=k, out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    log(f"bench: {ms_per_step * 1e3:.1f} us per step")
+    assert torch.isfinite(out).all().item(), "non-finite layer output"
+
+    # Dominant kernel: the gate/up GEMM, bracketed by events on its stream.
+    w0 = sets[0]
+    ids, tw = moe.route(x, w0["Wr"], w0["br"], k=k, workspace=ws)
+    counts, offsets, rows = moe.permute(ids, E, workspace=ws)
+    h = torch.empty((T * k, I), dtype=torch.int16, device=dev)
+    acc = torch.zeros((T, H), dtype=torch.float32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        w = sets[i % copies]
+        ids, tw = moe.route(x, w["Wr"], w["br"], k=k, workspace=ws, ids=ids, w=tw)
+        counts, offsets, rows = moe.permute(ids, E, workspace=ws)
+        j = i - args.warmup
+        if j >= 0:
+            evs[j][0].record(stream)
+        moe.gate_up(x, offsets, rows, w["w13_codes"], w["w13_scales"], w["b13"], k=k, h=h)
+        if j >= 0:
+            evs[j][1].record(stream)
+        moe.down_accumulate(h, offsets, rows, tw, w["w2_codes"], w["w2_scales"], w["b2"],
+                            out=acc, k=k)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    touched = int((counts > 0).sum().item())
+    log(f"bench: gate/up kernel {kern_ms * 1e3:.1f} us per launch, {touched} experts touched")
+
+    workload = f"{cfg.name} (E={E}, k={k})"
+    if cfg.regime == "decode":
+        alg = touched * W13_EXPERT_BYTES + T * H * 2 + T * k * I * 2
+        achieved = alg / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(workload),
+                "kernel": "ffn_skinny_kernel<EPI_SWIGLU> (gate/up + SwiGLU)",
+                "algorithmic_bytes_per_launch": alg}
+        layer_alg = touched * (W13_EXPERT_BYTES + W2_EXPERT_BYTES) + E * (H * 4 + 4) \
+            + T * H * 2 + T * H * 4 + T * k * 8
+        layer_frac = layer_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    else:
+        alg = 2.0 * T * k * H * 2 * I
+        achieved = alg / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(workload),
+                "kernel": "ffn_wide_kernel<EPI_SWIGLU> (gate/up + SwiGLU)",
+                "algorithmic_flop_per_launch": alg}
+        layer_flop = 2.0 * T * k * (H * 2 * I + H * I) + 2.0 * T * H * E
+        layer_frac = layer_flop / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+
+    res = {
+        "metric": METRIC,
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "T": T, "E": E, "k": k, "hidden": H,
+                   "intermediate": I, "weights": "MXFP4 (E2M1 + E8M0 per 32)",
+                   "weight_copies_rotated": copies, "seed": args.seed},
+        "roofline": roof,
+        "layer_roofline_frac": round(layer_frac, 4),
+        "experts_touched": touched,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens or (cfg.T if cfg.T <= 64 else (32 if E <= 32 else 16))
+        log(f"bench: oracle on {n} tokens")
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, n)
+    if args.copy_probe_mib:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = nbytes
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

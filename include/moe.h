@@ -32,14 +32,24 @@
  *   Outputs are fully overwritten.
  * - bf16 tensors are passed as uint16_t bit patterns. All tensors are
  *   row-major and contiguous; weights are [out_features, in_features].
- * - MXFP4 (OCP Microscaling v1.0): codes[n, b] holds two FP4 E2M1 codes, the
- *   low nibble for K = 2b and the high nibble for K = 2b + 1; scales[n, j] is
- *   an E8M0 byte s meaning 2^(s - 127) for K in [32j, 32j + 31]. Scale bytes
- *   in [2, 252] give exact bf16 weights; 255 (NaN) and the extremes are not
- *   supported (undefined results, never checked on the device).
+ * - MXFP4 (OCP Microscaling v1.0), checkpoint ("canonical") layout of a
+ *   weight [E, N, K = 2880]: codes [E, N, 1440] u8, byte b of a row holds two
+ *   FP4 E2M1 codes, the low nibble for K = 2b and the high nibble for
+ *   K = 2b + 1; scales [E, N, 90] u8, byte j is an E8M0 exponent s meaning
+ *   2^(s - 127) for K in [32j, 32j + 31]. Scale bytes in [2, 252] give exact
+ *   bf16 weights; 255 (NaN) and the extremes are not supported (undefined
+ *   results, never checked on the device).
+ * - The expert GEMMs read the weights in PACKED order, produced once per
+ *   weight tensor by moe_pack_weights (the "MXFP4 tensor packing" step named
+ *   in the techniques map's inference list; the order itself is this
+ *   library's). Packing permutes bytes inside each group of 64 rows only, so
+ *   the packed arrays have exactly the canonical sizes. Every w13_codes,
+ *   w13_scales, w2_codes, w2_scales argument below is packed.
  * - w13 rows are interleaved: row 2i is gate unit i, row 2i + 1 is up unit i.
- * - Alignment: x, Wr, out, y and every code array must be 16-byte aligned;
- *   otherwise MOE_ERROR_MISALIGNED. Other arrays need their natural alignment.
+ * - Alignment: x, Wr, out, y, h and every code array must be 16-byte aligned,
+ *   the bias arrays b13 / b2 8-byte aligned and every scale array 4-byte
+ *   aligned; otherwise MOE_ERROR_MISALIGNED. Other arrays need their natural
+ *   alignment.
  * - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *   and the call returns without synchronising. Calls on different streams
  *   are independent when they use different workspaces and outputs.
@@ -78,17 +88,34 @@ typedef enum moe_status {
  * Returns 0 when the sizes are out of range. */
 size_t moe_workspace_size(int T, int E, int k);
 
+/* Packs one MXFP4 weight tensor from the canonical layout into the order the
+ * expert GEMMs read (see the conventions above). N % 64 == 0, 64 <= N <= 65536,
+ * 1 <= E <= 256; K = 2880.
+ *   codes [E, N, 1440] u8, scales [E, N, 90] u8 (canonical, in)
+ *   packed_codes, packed_scales: same sizes (out; must not overlap the input)
+ * Packed order, per group G of rows [64G, 64G + 64) of one expert:
+ *   codes: 23 K steps s of four MX blocks (4s .. 4s + 3); step s holds four
+ *     16-row tiles m; tile m holds 64 lanes l = 16g + r of 16 bytes, lane l
+ *     carrying the codes of row 64G + 16m + r, block 4s + g. The last step
+ *     (blocks 88, 89) holds lanes 0..31 only: 512 bytes per tile.
+ *     offset = G*92160 + s*4096 + m*(s < 22 ? 1024 : 512) + l*16.
+ *   scales: offset = G*5760 + s*256 + l*4 + m for the same (s, m, l). */
+moe_status_t moe_pack_weights(const uint8_t* codes, const uint8_t* scales, int E, int N,
+                              uint8_t* packed_codes, uint8_t* packed_scales,
+                              void* stream);
+
 /* Router: logits = x Wr^T + br in fp32, then per token the k largest logits
  * (descending; equal logits -> lower expert id) and their softmax.
  *   x        [T, 2880] bf16      Wr [E, 2880] fp32     br [E] fp32
  *   topk_ids [T, k] int32 (out)  topk_w [T, k] fp32 (out)
  *   logits   [T, E] fp32 (out, optional: NULL to skip)
- * Source: techniques map rows "Mixture of experts" and "Auxiliary-loss-free
- * load balancing". */
+ * Uses the same kernels, in the same order, as moe_forward's routing, so both
+ * select the same experts. Source: techniques map rows "Mixture of experts"
+ * and "Auxiliary-loss-free load balancing". */
 moe_status_t moe_route(const uint16_t* x, const float* Wr, const float* br,
                        int T, int E, int k,
                        int32_t* topk_ids, float* topk_w, float* logits,
-                       void* stream);
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* Group the T*k routed slots by expert (counting sort, stable):
  *   counts[e]      number of slots routed to expert e            [E]
@@ -106,6 +133,7 @@ moe_status_t moe_permute(const int32_t* topk_ids, int T, int E, int k,
  *   offsets, sorted_rows   as produced by moe_permute
  *   w13_codes [E, 5760, 1440] u8   w13_scales [E, 5760, 90] u8   b13 [E, 5760] bf16
  *   w2_codes  [E, 2880, 1440] u8   w2_scales  [E, 2880, 90] u8   b2  [E, 2880] bf16
+ *   (codes and scales packed by moe_pack_weights)
  *   y [T*k, 2880] fp32 (out)
  * The gate/up intermediate h is rounded to bf16 (the matrix-core input type).
  * Source: techniques map row "SwiGLU feed-forward"; swiglu_limit from the raw
@@ -118,6 +146,34 @@ moe_status_t moe_expert_ffn(const uint16_t* x, const int32_t* offsets,
                             const uint16_t* b2,
                             int T, int E, int k, float* y,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* The two halves of moe_expert_ffn / moe_forward as separate calls.
+ *
+ * moe_gate_up: gate/up projection and SwiGLU of every routed slot, in
+ * expert-sorted order:
+ *   h[p, :] = bf16( SwiGLU( W13[e] x[t] + b13[e] ) ),  t = sorted_rows[p] / k,
+ *   e = the expert whose range [offsets[e], offsets[e+1]) contains p.
+ *   h [T*k, 2880] bf16 (out). Source: techniques map row "SwiGLU feed-forward".
+ *
+ * moe_down_accumulate: down projection of h, weighted by the routing weight
+ * and ADDED into out:
+ *   out[t, :] += topk_w[s] * ( W2[e] h[p, :] + b2[e] ),  s = sorted_rows[p], t = s / k
+ *   out [T, 2880] fp32 is accumulated, not overwritten: pass zeros for the
+ *   layer output, or the residual stream to fold the residual add in. The
+ *   order in which a token's k contributions are added is not fixed (atomic
+ *   adds), so results may differ in the last bits from run to run.
+ *   Source: techniques map, "Mixture of experts" (weighted sum of experts). */
+moe_status_t moe_gate_up(const uint16_t* x, const int32_t* offsets,
+                         const int32_t* sorted_rows,
+                         const uint8_t* w13_codes, const uint8_t* w13_scales,
+                         const uint16_t* b13, int T, int E, int k,
+                         uint16_t* h, void* stream);
+
+moe_status_t moe_down_accumulate(const uint16_t* h, const int32_t* offsets,
+                                 const int32_t* sorted_rows, const float* topk_w,
+                                 const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                 const uint16_t* b2, int T, int E, int k,
+                                 float* out, void* stream);
 
 /* out[t, :] = sum_j topk_w[t, j] * y[t*k + j, :]
  *   y [T*k, 2880] fp32, topk_w [T, k] fp32, out [T, 2880] fp32 (out).

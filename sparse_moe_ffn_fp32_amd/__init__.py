@@ -20,8 +20,8 @@ from . import _native
 H = 2880
 I = 2880
 
-__all__ = ["MoeError", "workspace_size", "route", "permute", "expert_ffn", "combine",
-           "forward", "H", "I"]
+__all__ = ["MoeError", "workspace_size", "pack_weights", "pack_expert_weights", "route", "permute", "expert_ffn", "gate_up",
+           "down_accumulate", "combine", "forward", "H", "I"]
 
 
 class MoeError(RuntimeError):
@@ -92,19 +92,42 @@ def _weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2):
     return E
 
 
+def pack_weights(codes: torch.Tensor, scales: torch.Tensor):
+    """Canonical MXFP4 codes [E,N,1440] / scales [E,N,90] -> packed copies (same shapes)."""
+    E, N = codes.shape[0], codes.shape[1]
+    _dev(codes, "codes", _U8, (E, N, H // 2))
+    _dev(scales, "scales", _U8, (E, N, H // 32))
+    pc = torch.empty_like(codes)
+    ps = torch.empty_like(scales)
+    _check(_native.lib().moe_pack_weights(_ptr(codes), _ptr(scales), E, N, _ptr(pc), _ptr(ps),
+                                          _stream(codes)), "moe_pack_weights")
+    return pc, ps
+
+
+def pack_expert_weights(w13_codes, w13_scales, w2_codes, w2_scales):
+    """Both expert weight tensors -> (w13_codes, w13_scales, w2_codes, w2_scales) packed."""
+    return (*pack_weights(w13_codes, w13_scales), *pack_weights(w2_codes, w2_scales))
+
+
 def route(x: torch.Tensor, Wr: torch.Tensor, br: torch.Tensor, k: int = 4,
-          return_logits: bool = False):
+          return_logits: bool = False, workspace: Optional[torch.Tensor] = None,
+          ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None):
     """-> (topk_ids int32 [T,k], topk_w fp32 [T,k][, logits fp32 [T,E]])"""
     T = x.shape[0]
     E = Wr.shape[0]
     _dev(x, "x", _BF16, (T, H))
     _dev(Wr, "Wr", _F32, (E, H))
     _dev(br, "br", _F32, (E,))
-    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
-    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _dev(ids, "ids", _I32, (T, k))
+    _dev(w, "w", _F32, (T, k))
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if return_logits else None
+    ws = _workspace(T, E, k, x.device, workspace)
     _check(_native.lib().moe_route(_ptr(x), _ptr(Wr), _ptr(br), T, E, k, _ptr(ids), _ptr(w),
-                                   _ptr(logits), _stream(x)), "moe_route")
+                                   _ptr(logits), _ptr(ws), ws.numel(), _stream(x)), "moe_route")
     return (ids, w, logits) if return_logits else (ids, w)
 
 
@@ -138,6 +161,47 @@ def expert_ffn(x, offsets, sorted_rows, w13_codes, w13_scales, b13, w2_codes, w2
         _ptr(w2_codes), _ptr(w2_scales), _ptr(b2), T, E, k, _ptr(y), _ptr(ws), ws.numel(),
         _stream(x)), "moe_expert_ffn")
     return y
+
+
+def gate_up(x, offsets, sorted_rows, w13_codes, w13_scales, b13, k: int = 4,
+            h: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """-> h bf16 [T*k, 2880] (as int16 bits), SwiGLU of the gate/up projection
+    of every routed slot, in expert-sorted order."""
+    T = x.shape[0]
+    E = w13_codes.shape[0]
+    _dev(x, "x", _BF16, (T, H))
+    _dev(w13_codes, "w13_codes", _U8, (E, 2 * I, H // 2))
+    _dev(w13_scales, "w13_scales", _U8, (E, 2 * I, H // 32))
+    _dev(b13, "b13", _BF16, (E, 2 * I))
+    _dev(offsets, "offsets", _I32, (E + 1,))
+    _dev(sorted_rows, "sorted_rows", _I32, (T * k,))
+    if h is None:
+        h = torch.empty((T * k, I), dtype=torch.int16, device=x.device)
+    else:
+        _dev(h, "h", _BF16, (T * k, I))
+    _check(_native.lib().moe_gate_up(
+        _ptr(x), _ptr(offsets), _ptr(sorted_rows), _ptr(w13_codes), _ptr(w13_scales), _ptr(b13),
+        T, E, k, _ptr(h), _stream(x)), "moe_gate_up")
+    return h
+
+
+def down_accumulate(h, offsets, sorted_rows, topk_w, w2_codes, w2_scales, b2,
+                    out: torch.Tensor, k: int = 4) -> torch.Tensor:
+    """out[t] += sum_j topk_w[t, j] * (W2[e] h + b2[e]) over the slots of t; returns out."""
+    T = out.shape[0]
+    E = w2_codes.shape[0]
+    _dev(out, "out", _F32, (T, H))
+    _dev(h, "h", _BF16, (T * k, I))
+    _dev(topk_w, "topk_w", _F32)
+    _dev(w2_codes, "w2_codes", _U8, (E, H, I // 2))
+    _dev(w2_scales, "w2_scales", _U8, (E, H, I // 32))
+    _dev(b2, "b2", _BF16, (E, H))
+    _dev(offsets, "offsets", _I32, (E + 1,))
+    _dev(sorted_rows, "sorted_rows", _I32, (T * k,))
+    _check(_native.lib().moe_down_accumulate(
+        _ptr(h), _ptr(offsets), _ptr(sorted_rows), _ptr(topk_w), _ptr(w2_codes), _ptr(w2_scales),
+        _ptr(b2), T, E, k, _ptr(out), _stream(out)), "moe_down_accumulate")
+    return out
 
 
 def combine(y: torch.Tensor, topk_w: torch.Tensor) -> torch.Tensor:

@@ -12,8 +12,9 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmoe_mi355x.so")
 
 # every symbol declared in include/moe.h
-EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
-            "moe_combine", "moe_forward", "moe_status_string")
+EXPORTED = ("moe_workspace_size", "moe_pack_weights", "moe_route", "moe_permute", "moe_expert_ffn",
+            "moe_gate_up", "moe_down_accumulate", "moe_combine", "moe_forward",
+            "moe_status_string")
 
 MOE_SUCCESS = 0
 STATUS_NAMES = {
@@ -46,12 +47,18 @@ def lib() -> ctypes.CDLL:
     L.moe_workspace_size.restype = SZ
     L.moe_status_string.argtypes = [ST]
     L.moe_status_string.restype = ctypes.c_char_p
-    L.moe_route.argtypes = [P, P, P, I, I, I, P, P, P, P]
+    L.moe_pack_weights.argtypes = [P, P, I, I, P, P, P]
+    L.moe_pack_weights.restype = ST
+    L.moe_route.argtypes = [P, P, P, I, I, I, P, P, P, P, SZ, P]
     L.moe_route.restype = ST
     L.moe_permute.argtypes = [P, I, I, I, P, P, P, P, SZ, P]
     L.moe_permute.restype = ST
     L.moe_expert_ffn.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, P, SZ, P]
     L.moe_expert_ffn.restype = ST
+    L.moe_gate_up.argtypes = [P, P, P, P, P, P, I, I, I, P, P]
+    L.moe_gate_up.restype = ST
+    L.moe_down_accumulate.argtypes = [P, P, P, P, P, P, P, I, I, I, P, P]
+    L.moe_down_accumulate.restype = ST
     L.moe_combine.argtypes = [P, P, I, I, P, P]
     L.moe_combine.restype = ST
     L.moe_forward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, P, P, SZ, P]

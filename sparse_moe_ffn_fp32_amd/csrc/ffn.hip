@@ -1,4 +1,4 @@
-// Grouped expert GEMMs over MXFP4 weights with fused epilogues.
+// Grouped expert GEMMs over packed MXFP4 weights with fused epilogues.
 //
 // Gate/up: gu = x W13[e]^T + b13[e], then the gpt-oss gated unit
 //   h = (clamp(up, -7, 7) + 1) * min(gate, 7) * sigmoid(1.702 * min(gate, 7))
@@ -9,140 +9,241 @@
 // sum over the selected experts, row "Mixture of experts").
 //
 // Weights are MXFP4 (techniques map, "inference & serving": MXFP4 weight
-// quantization / tensor packing): a lane loads one whole 32-element block (16
-// code bytes, one 128-bit load) plus its E8M0 byte and converts it to bf16 in
-// registers with v_cvt_scalef32_pk_bf16_fp4, which is exact for the scale
-// range the library supports. Products run on bf16 matrix cores with fp32
-// accumulation. The K index assignment inside a matrix-core step is free as
-// long as both operands agree: a lane's 32 weight values (one block) meet the
-// 32 activation values of the same K range.
+// quantization, MXFP4 tensor packing) in the library's packed order (see
+// moe_pack_weights in moe.h): inside each group of 64 rows, the bytes come in
+// the order the matrix-core lanes consume them, so every weight load of a wave
+// is one contiguous, fully coalesced 1 KiB (16 code bytes per lane). A lane
+// l = 16g + r holds row r of a 16-row tile and MX block 4s + g of K step s,
+// converts its 32 codes to bf16 in registers (v_cvt_scalef32_pk_bf16_fp4,
+// exact for the supported scales) and feeds four 16x16x32 bf16 MFMAs (fp32
+// accumulate). The activation operand supplies the same K range for lane
+// group g, so each MFMA sums over 8 consecutive K of 4 blocks.
 //
 // Two schedules:
-//  * weight-streaming ("skinny"), for few rows per expert (decode): one wave
-//    owns 64 weight rows of one expert and <= 16 of its tokens, streams the
-//    rows' blocks with a 3-step register prefetch and reads its activations
-//    straight from global memory (L2-resident). 16x16x32 bf16 MFMA with the
-//    weights as the 16-row operand.
-//  * tiled ("wide"), for many rows per expert (prefill): a 256-thread block
-//    owns 256 weight rows x 128 tokens; the gathered activation tile goes
-//    through a double-buffered LDS ring (64 K per step), weights go straight
-//    to registers. 32x32x16 bf16 MFMA.
+//  * weight-streaming ("skinny", few rows per expert: decode). One wave owns
+//    one or two 64-row groups of one expert and its tokens, 16 at a time;
+//    it streams the groups' code bytes front to back with a 3-step register
+//    prefetch and reads its activations directly (L2-resident).
+//  * tiled ("wide", many rows per expert: prefill). A 256-thread block owns
+//    four 64-row groups x 128 tokens; the gathered activation tile goes
+//    through a double-buffered LDS ring (128 K per step), weights straight to
+//    registers as above.
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace moe {
 
-// ------------------------------------------------------------------ skinny
-constexpr int kSkRows = 64;    // weight rows per wave (four 16-row tiles)
-constexpr int kSkBT = 16;      // tokens per tile
-constexpr int kSkSteps = 23;   // ceil(90 blocks / 4 lane groups)
-constexpr int kSkDepth = 3;    // prefetch depth in steps
+// ------------------------------------------------------------------ packing
+// canonical [E, N, 1440] codes + [E, N, 90] scales -> packed order (a byte
+// permutation inside every 64-row group). One thread per (row, MX block).
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes,
+                                                   const uint8_t* __restrict__ scales,
+                                                   long long units, uint8_t* __restrict__ pcodes,
+                                                   uint8_t* __restrict__ pscales) {
+  const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int kb = (int)(u % kKB);
+  const long long row = u / kKB;         // e * N + n
+  const long long grp = row >> 6;
+  const int rin = (int)(row & 63);
+  const int m = rin >> 4, r = rin & 15;
+  const int s = kb >> 2, g = kb & 3;
+  const int l = 16 * g + r;
+  const long long dst = grp * kGroupCodeBytes + (long long)s * kStepCodeBytes +
+                        m * (s < kFullSteps ? 1024 : 512) + l * 16;
+  *reinterpret_cast<uint4*>(pcodes + dst) = *reinterpret_cast<const uint4*>(codes + u * 16);
+  pscales[grp * kGroupScaleBytes + s * 256 + l * 4 + m] = scales[u];
+}
 
-struct SkStage {
-  uint4 w[4];
-  uint32_t sc[4];
-  uint4 xv[4];
-};
+hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, int E, int N,
+                       uint8_t* pcodes, uint8_t* pscales, hipStream_t s) {
+  const long long units = (long long)E * N * kKB;
+  const unsigned blocks = (unsigned)((units + 255) / 256);
+  hipLaunchKernelGGL(pack_kernel, dim3(blocks), dim3(256), 0, s, codes, scales, units, pcodes, pscales);
+  return hipGetLastError();
+}
 
-template <int EPI>
-__global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
-  const int lane = threadIdx.x;
-  int e, rb, re;
-  if (!find_tile(a.offsets, a.E, kSkBT, blockIdx.y, e, rb, re)) return;
-  const int row_base = blockIdx.x * kSkRows;
-  const int r = lane & 15;   // weight row in a 16-row tile / token column
-  const int g = lane >> 4;   // lane group: owns MX block 4s + g in step s
-  const int p = rb + r;
-  const bool tok_ok = p < re;
-  const int slot = tok_ok ? a.sorted_rows[p] : 0;
-  const int arow = a.gather ? slot / a.k : p;
-  const uint16_t* xp = a.act + (size_t)(tok_ok ? arow : 0) * kH;
-  const size_t wrow0 = (size_t)e * a.N + row_base + r;
-  const uint8_t* cp = a.codes + wrow0 * kRowCodeBytes;
-  const uint8_t* sp = a.scales + wrow0 * kRowScaleBytes;
+// Weight fragment loader of one wave over one packed 64-row group. Loads are
+// unconditional (branch-free, so the compiler can count outstanding loads
+// exactly): in the half last step, lanes 32..63 re-read lanes 0..31's bytes
+// and their codes are replaced by zeros.
+struct GroupStream {
+  const uint8_t* cg;   // codes of the group + lane * 16
+  const uint8_t* sg;   // scales of the group + lane * 4
+  bool half_ok;        // lane group g < 2: valid in the last (half) step
 
-  auto issue = [&](SkStage& st, int s) {
-    const int kb = 4 * s + g;
-    const bool k_ok = kb < kKB;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      st.w[mt] = make_uint4(0, 0, 0, 0);
-      st.sc[mt] = 127;
-      if (k_ok) {
-        st.w[mt] = *reinterpret_cast<const uint4*>(cp + (size_t)mt * 16 * kRowCodeBytes + kb * 16);
-        st.sc[mt] = sp[(size_t)mt * 16 * kRowScaleBytes + kb];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st.xv[i] = make_uint4(0, 0, 0, 0);
-      if (k_ok && tok_ok) st.xv[i] = *reinterpret_cast<const uint4*>(xp + kb * 32 + 8 * i);
-    }
-  };
+  __device__ __forceinline__ void init(const FfnArgs& a, int e, int G, int lane) {
+    const size_t grp = (size_t)e * (a.N >> 6) + G;
+    const int l_last = lane & 31;
+    cg = a.codes + grp * kGroupCodeBytes;
+    sg = a.scales + grp * kGroupScaleBytes;
+    half_ok = (lane >> 4) < 2;
+    lane_c = lane * 16;
+    lane_c_last = l_last * 16;
+    lane_s = lane * 4;
+    lane_s_last = l_last * 4;
+  }
+  int lane_c, lane_c_last, lane_s, lane_s_last;
 
-  f32x4 acc[4];
+  // four 16-row tiles of step s (s is a compile-time constant after unrolling)
+  __device__ __forceinline__ void load(int s, uint4 (&w)[4], uint32_t& sc) const {
+    const bool last = s >= kFullSteps;
+    const int tstride = last ? 512 : 1024;
+    const uint8_t* c = cg + s * kStepCodeBytes + (last ? lane_c_last : lane_c);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const SkStage& st) {
-    float sf[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sf[mt] = e8m0_to_f32(st.sc[mt]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x8 xb = u4_as_bf16x8(st.xv[i]);
+    for (int mt = 0; mt < 4; ++mt) w[mt] = *reinterpret_cast<const uint4*>(c + mt * tstride);
+    sc = *reinterpret_cast<const uint32_t*>(sg + s * 256 + (last ? lane_s_last : lane_s));
+    if (last) {
+      const uint32_t keep = half_ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const uint32_t wd = i == 0 ? st.w[mt].x : i == 1 ? st.w[mt].y : i == 2 ? st.w[mt].z : st.w[mt].w;
-        const bf16x8 wb = fp4x8_to_bf16x8(wd, sf[mt]);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, acc[mt], 0, 0, 0);
-      }
-    }
-  };
-
-  SkStage st[kSkDepth];
-#pragma unroll
-  for (int q = 0; q < kSkDepth; ++q) issue(st[q], q);
-  for (int s0 = 0; s0 < kSkSteps; s0 += kSkDepth) {
-#pragma unroll
-    for (int q = 0; q < kSkDepth; ++q) {
-      const int s = s0 + q;
-      if (s < kSkSteps) {
-        compute(st[q]);
-        if (s + kSkDepth < kSkSteps) issue(st[q], s + kSkDepth);
+        w[mt].x &= keep; w[mt].y &= keep; w[mt].z &= keep; w[mt].w &= keep;
       }
     }
   }
+};
 
-  // 16x16 result: lane holds token column r and weight rows 4g + j.
-  const uint16_t* bias = a.bias + (size_t)e * a.N;
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// ------------------------------------------------------------------ skinny
+constexpr int kSkBT = 16;      // tokens per tile
+constexpr int kSkDepth = 3;    // prefetch depth in K steps
+
+template <int RG>
+struct SkStage {
+  uint4 w[4 * RG];
+  uint32_t sc[RG];
+  uint4 xv[4];
+};
+
+// Grid (RG consecutive 64-row groups, expert e). One wave streams RG groups
+// (64*RG rows: the activations it reads are shared by all of them). The
+// weight stream needs no routing data, so the wave only waits for the
+// expert's row range and its first row lookups before the stream starts; a
+// dependent load issued behind the chip-wide weight traffic would wait for
+// the whole in-flight volume. An expert with more than 16 rows is handled 16
+// at a time.
+template <int EPI, int RG>
+__global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
+  constexpr int MT = 4 * RG;
+  const int lane = threadIdx.x;
+  const int G0 = blockIdx.x * RG;
+  const int e = blockIdx.y;
+  const int r = lane & 15;   // weight row in a 16-row tile / token column
+  const int g = lane >> 4;   // lane group: MX block 4s + g of step s
+  const int e_begin = a.offsets[e];
+  const int e_end = a.offsets[e + 1];
+  if (e_end <= e_begin) return;
+  // biases of this lane's output rows (consumed by the epilogue)
+  const uint16_t* bias = a.bias + (size_t)e * a.N + G0 * 64 + 4 * g;
+  uint2 braw[MT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int R0 = row_base + 16 * mt + 4 * g;
-    float v[4];
+  for (int mt = 0; mt < MT; ++mt) braw[mt] = *reinterpret_cast<const uint2*>(bias + 16 * mt);
+
+  for (int rb = e_begin; rb < e_end; rb += kSkBT) {
+    const int re = min(e_end, rb + kSkBT);
+    const int p = rb + r;
+    const bool tok_ok = p < re;
+    // padded token columns read the tile's first row: their outputs are dropped
+    const int slot = a.sorted_rows[tok_ok ? p : rb];
+    const int arow = a.gather ? slot / a.k : (tok_ok ? p : rb);
+    const uint16_t* xp = a.act + (size_t)arow * kH;
+    // slot >= 0 always; the compiler cannot know it, so the weight addresses
+    // depend on the row lookup and the stream starts after it returns
+    GroupStream ws[RG];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = acc[mt][j] + bf16_bits_to_f32(bias[R0 + j]);
-    if (!tok_ok) continue;
-    if constexpr (EPI == EPI_SWIGLU) {
-      const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(v[0], v[1]));
-      const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(v[2], v[3]));
-      *reinterpret_cast<uint32_t*>(a.h_out + (size_t)p * kI + R0 / 2) = h0 | (h1 << 16);
-    } else if constexpr (EPI == EPI_COMBINE) {
-      const float wt = a.topk_w[slot];
-      float* o = a.out + (size_t)(slot / a.k) * kH + R0;
+    for (int q = 0; q < RG; ++q) ws[q].init(a, e + (slot < 0 ? 1 : 0), G0 + q, lane);
+
+    // s is a compile-time constant after unrolling; the K tail (blocks >= 90)
+    // re-reads block 89, whose weights are zero there
+    auto issue = [&](SkStage<RG>& st, int s) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) unsafeAtomicAdd(o + j, wt * v[j]);
-    } else {
-      *reinterpret_cast<float4*>(a.y_out + (size_t)slot * kH + R0) = make_float4(v[0], v[1], v[2], v[3]);
+      for (int q = 0; q < RG; ++q) {
+        uint4 w4[4];
+        ws[q].load(s, w4, st.sc[q]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) st.w[4 * q + mt] = w4[mt];
+      }
+      const int kb = min(4 * s + g, kKB - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.xv[i] = *reinterpret_cast<const uint4*>(xp + kb * 32 + 8 * i);
+    };
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const SkStage<RG>& st) __attribute__((always_inline)) {
+      float sf[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) sf[mt] = e8m0_to_f32((st.sc[mt / 4] >> (8 * (mt % 4))) & 0xFFu);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 xb = u4_as_bf16x8(st.xv[i]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 wb = fp4x8_to_bf16x8(dword_of(st.w[mt], i), sf[mt]);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, acc[mt], 0, 0, 0);
+        }
+      }
+    };
+
+    // fully unrolled K loop with a kSkDepth-step register prefetch ring
+    SkStage<RG> st[kSkDepth];
+#pragma unroll
+    for (int q = 0; q < kSkDepth; ++q) issue(st[q], q);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      compute(st[s % kSkDepth]);
+      if (s + kSkDepth < kSteps) issue(st[s % kSkDepth], s + kSkDepth);
+    }
+
+    // 16x16 result: lane holds token column r and weight rows 4g + j of each tile.
+    if (tok_ok) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int R0 = G0 * 64 + 16 * mt + 4 * g;
+        const float v0 = acc[mt][0] + bf16_bits_to_f32(braw[mt].x & 0xFFFFu);
+        const float v1 = acc[mt][1] + bf16_bits_to_f32(braw[mt].x >> 16);
+        const float v2 = acc[mt][2] + bf16_bits_to_f32(braw[mt].y & 0xFFFFu);
+        const float v3 = acc[mt][3] + bf16_bits_to_f32(braw[mt].y >> 16);
+        if constexpr (EPI == EPI_SWIGLU) {
+          const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(v0, v1));
+          const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(v2, v3));
+          *reinterpret_cast<uint32_t*>(a.h_out + (size_t)p * kI + R0 / 2) = h0 | (h1 << 16);
+        } else if constexpr (EPI == EPI_COMBINE) {
+          const float wt = a.topk_w[slot];
+          float* o = a.out + (size_t)(slot / a.k) * kH + R0;
+          unsafeAtomicAdd(o + 0, wt * v0);
+          unsafeAtomicAdd(o + 1, wt * v1);
+          unsafeAtomicAdd(o + 2, wt * v2);
+          unsafeAtomicAdd(o + 3, wt * v3);
+        } else {
+          *reinterpret_cast<float4*>(a.y_out + (size_t)slot * kH + R0) = make_float4(v0, v1, v2, v3);
+        }
+      }
     }
   }
 }
 
+// Two groups per wave halve the activation reads per weight byte, but only
+// pay off while enough waves remain in flight: the gate/up GEMM (90 groups
+// per expert) takes two, the down GEMM (45) one.
+template <int EPI>
+static void launch_skinny(const FfnArgs& a, hipStream_t s) {
+  const int groups = a.N >> 6;
+  if (groups % 2 == 0 && groups >= 90)
+    hipLaunchKernelGGL((ffn_skinny_kernel<EPI, 2>), dim3(groups / 2, a.E), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((ffn_skinny_kernel<EPI, 1>), dim3(groups, a.E), dim3(64), 0, s, a);
+}
+
 // ------------------------------------------------------------------ wide
-constexpr int kWdBT = 128;      // tokens per tile
-constexpr int kWdRows = 256;    // weight rows per block (4 waves x 64)
-constexpr int kWdSteps = 45;    // K = 2880 in steps of 64 (two MX blocks)
-constexpr int kXsStride = 72;   // bf16 per LDS activation row (64 + 8 pad)
+constexpr int kWdBT = 128;     // tokens per tile (8 column tiles of 16)
+constexpr int kWdGroups = 4;   // 64-row groups per block, one per wave
+constexpr int kXsStride = 136; // bf16 per LDS activation row (128 K + 8 pad)
 
 template <int EPI, bool W_AS_B>
 __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
@@ -153,87 +254,76 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
   const int wave = tid >> 6;
   int e, rb, re;
   if (!find_tile(a.offsets, a.E, kWdBT, blockIdx.y, e, rb, re)) return;
-  const int row_w = blockIdx.x * kWdRows + wave * 64;
-  const bool w_ok = row_w < a.N;
+  const int G = blockIdx.x * kWdGroups + wave;
+  const bool w_ok = G < (a.N >> 6);
   if (tid < kWdBT) {
     const int p = rb + tid;
     slot_of[tid] = p < re ? a.sorted_rows[p] : -1;
   }
 
-  // activation loader: chunk c = tid + 256q -> token (tid >> 3) + 32q, 16-byte piece tid & 7
-  const int piece = tid & 7;
-  const uint16_t* gptr[4];
-  bool gok[4];
+  // activation loader: chunk c = tid + 256q -> token (tid >> 4) + 16q, 16-byte
+  // piece tid & 15; padded tokens and the K tail are zero-filled
+  const int piece = tid & 15;
+  const uint16_t* gptr[8];
+  bool gok[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int tt = (tid >> 3) + 32 * q;
-    const int p = rb + tt;
+  for (int q = 0; q < 8; ++q) {
+    const int p = rb + (tid >> 4) + 16 * q;
     gok[q] = p < re;
     int row = 0;
     if (gok[q]) row = a.gather ? a.sorted_rows[p] / a.k : p;
     gptr[q] = a.act + (size_t)row * kH + piece * 8;
   }
-  uint4 xr[4];
-  auto load_x = [&](int s) {
+  uint4 xr[8];
+  auto load_x = [&](int s) __attribute__((always_inline)) {
+    const bool kok = (s < kFullSteps) || piece < 8;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 8; ++q) {
       xr[q] = make_uint4(0, 0, 0, 0);
-      if (gok[q]) xr[q] = *reinterpret_cast<const uint4*>(gptr[q] + s * 64);
+      if (gok[q] && kok) xr[q] = *reinterpret_cast<const uint4*>(gptr[q] + s * 128);
     }
   };
-  auto store_x = [&](int stage) {
+  auto store_x = [&](int stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int tt = (tid >> 3) + 32 * q;
+    for (int q = 0; q < 8; ++q) {
+      const int tt = (tid >> 4) + 16 * q;
       *reinterpret_cast<uint4*>(&xs[stage][tt * kXsStride + piece * 8]) = xr[q];
     }
   };
 
-  // weight rows of this wave: tile mt covers rows row_w + 32mt + (lane & 31)
-  const int r32 = lane & 31;
-  const int hh = lane >> 5;   // lane half: owns MX block 2s + hh in step s
-  const size_t wrow0 = (size_t)e * a.N + (w_ok ? row_w : 0) + r32;
-  const uint8_t* cp = a.codes + wrow0 * kRowCodeBytes;
-  const uint8_t* sp = a.scales + wrow0 * kRowScaleBytes;
-  uint4 wq[2][2];
-  uint32_t wsc[2][2];
-  auto load_w = [&](int buf, int s) {
-    const int kb = 2 * s + hh;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      wq[buf][mt] = *reinterpret_cast<const uint4*>(cp + (size_t)mt * 32 * kRowCodeBytes + kb * 16);
-      wsc[buf][mt] = sp[(size_t)mt * 32 * kRowScaleBytes + kb];
-    }
-  };
+  GroupStream wsrc;
+  wsrc.init(a, e, w_ok ? G : 0, lane);
+  uint4 wq[2][4];
+  uint32_t wsc[2];
+  const int r = lane & 15;
+  const int g = lane >> 4;
 
-  f32x16 acc[2][4];
+  f32x4 acc[4][8];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16{};
+    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int stage, int buf) {
+  auto compute = [&](int stage, int buf) __attribute__((always_inline)) {
     const uint16_t* xsb = xs[stage];
-    float sf[2];
+    float sf[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) sf[mt] = e8m0_to_f32(wsc[buf][mt]);
+    for (int mt = 0; mt < 4; ++mt) sf[mt] = e8m0_to_f32((wsc[buf] >> (8 * mt)) & 0xFFu);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      bf16x8 xf[4];
+      bf16x8 xf[8];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        xf[nt] = *reinterpret_cast<const bf16x8*>(&xsb[(32 * nt + r32) * kXsStride + 32 * hh + 8 * i]);
+      for (int nt = 0; nt < 8; ++nt)
+        xf[nt] = *reinterpret_cast<const bf16x8*>(&xsb[(16 * nt + r) * kXsStride + 32 * g + 8 * i]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const uint4 w4 = wq[buf][mt];
-        const uint32_t wd = i == 0 ? w4.x : i == 1 ? w4.y : i == 2 ? w4.z : w4.w;
-        const bf16x8 wf = fp4x8_to_bf16x8(wd, sf[mt]);
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 wf = fp4x8_to_bf16x8(dword_of(wq[buf][mt], i), sf[mt]);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < 8; ++nt) {
           if constexpr (W_AS_B)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[nt], wf, acc[mt][nt], 0, 0, 0);
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[nt], wf, acc[mt][nt], 0, 0, 0);
           else
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf[nt], acc[mt][nt], 0, 0, 0);
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[nt], acc[mt][nt], 0, 0, 0);
         }
       }
     }
@@ -243,20 +333,21 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
   store_x(0);
   load_x(1);
   if (w_ok) {
-    load_w(0, 0);
-    load_w(1, 1);
+    wsrc.load(0, wq[0], wsc[0]);
+    wsrc.load(1, wq[1], wsc[1]);
   }
   __syncthreads();
-  for (int s0 = 0; s0 < kWdSteps; s0 += 2) {
+  // K loop, unrolled by two: LDS activation ring of 2, register weight ring of 2
+  for (int s0 = 0; s0 < kSteps; s0 += 2) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int s = s0 + q;
-      if (s < kWdSteps) {
-        if (s + 1 < kWdSteps) store_x(q ^ 1);
-        if (s + 2 < kWdSteps) load_x(s + 2);
+      if (s < kSteps) {
+        if (s + 1 < kSteps) store_x(q ^ 1);
+        if (s + 2 < kSteps) load_x(s + 2);
         if (w_ok) {
           compute(q, q);
-          if (s + 2 < kWdSteps) load_w(q, s + 2);
+          if (s + 2 < kSteps) wsrc.load(s + 2, wq[q], wsc[q]);
         }
         __syncthreads();
       }
@@ -266,47 +357,41 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
 
   const uint16_t* bias = a.bias + (size_t)e * a.N;
   if constexpr (!W_AS_B) {
-    // D[weight row][token]: lane holds token column r32, rows 8q + 4hh + j
+    // D[weight row][token]: lane holds token column r, rows 4g + j of tile mt
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 4; ++mt) {
+      const int R0 = G * 64 + 16 * mt + 4 * g;
+      float b[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int R0 = row_w + 32 * mt + 8 * q + 4 * hh;
-        float b[4];
+      for (int j = 0; j < 4; ++j) b[j] = bf16_bits_to_f32(bias[R0 + j]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = bf16_bits_to_f32(bias[R0 + j]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int p = rb + 32 * nt + r32;
-          if (p >= re) continue;
-          const f32x16& c = acc[mt][nt];
-          const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(c[4 * q] + b[0], c[4 * q + 1] + b[1]));
-          const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(c[4 * q + 2] + b[2], c[4 * q + 3] + b[3]));
-          *reinterpret_cast<uint32_t*>(a.h_out + (size_t)p * kI + R0 / 2) = h0 | (h1 << 16);
-        }
+      for (int nt = 0; nt < 8; ++nt) {
+        const int p = rb + 16 * nt + r;
+        if (p >= re) continue;
+        const f32x4& c = acc[mt][nt];
+        const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(c[0] + b[0], c[1] + b[1]));
+        const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(c[2] + b[2], c[3] + b[3]));
+        *reinterpret_cast<uint32_t*>(a.h_out + (size_t)p * kI + R0 / 2) = h0 | (h1 << 16);
       }
     }
   } else {
-    // D[token][weight row]: lane holds weight row (output feature) r32,
-    // tokens 8q + 4hh + j of the 32-token tile
+    // D[token][weight row]: lane holds weight row (output feature) r of tile
+    // mt, tokens 4g + j of column tile nt
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int f = row_w + 32 * mt + r32;
+    for (int mt = 0; mt < 4; ++mt) {
+      const int f = G * 64 + 16 * mt + r;
       const float bf = bf16_bits_to_f32(bias[f]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int slot = slot_of[32 * nt + 8 * q + 4 * hh + j];
-            if (slot < 0) continue;
-            const float v = acc[mt][nt][4 * q + j] + bf;
-            if constexpr (EPI == EPI_COMBINE) {
-              unsafeAtomicAdd(a.out + (size_t)(slot / a.k) * kH + f, a.topk_w[slot] * v);
-            } else {
-              a.y_out[(size_t)slot * kH + f] = v;
-            }
+        for (int j = 0; j < 4; ++j) {
+          const int slot = slot_of[16 * nt + 4 * g + j];
+          if (slot < 0) continue;
+          const float v = acc[mt][nt][j] + bf;
+          if constexpr (EPI == EPI_COMBINE) {
+            unsafeAtomicAdd(a.out + (size_t)(slot / a.k) * kH + f, a.topk_w[slot] * v);
+          } else {
+            a.y_out[(size_t)slot * kH + f] = v;
           }
         }
       }
@@ -318,18 +403,17 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
 constexpr int kSkinnyMaxMeanRows = 24;
 
 hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s) {
+  const int groups = a.N >> 6;
   const bool skinny = (long long)n_rows <= (long long)kSkinnyMaxMeanRows * a.E;
   if (skinny) {
-    const int tiles = (n_rows + kSkBT - 1) / kSkBT + min(a.E, n_rows);
-    const dim3 grid(a.N / kSkRows, tiles);
     switch (epi) {
-      case EPI_SWIGLU: hipLaunchKernelGGL(ffn_skinny_kernel<EPI_SWIGLU>, grid, dim3(64), 0, s, a); break;
-      case EPI_COMBINE: hipLaunchKernelGGL(ffn_skinny_kernel<EPI_COMBINE>, grid, dim3(64), 0, s, a); break;
-      default: hipLaunchKernelGGL(ffn_skinny_kernel<EPI_STORE_Y>, grid, dim3(64), 0, s, a); break;
+      case EPI_SWIGLU: launch_skinny<EPI_SWIGLU>(a, s); break;
+      case EPI_COMBINE: launch_skinny<EPI_COMBINE>(a, s); break;
+      default: launch_skinny<EPI_STORE_Y>(a, s); break;
     }
   } else {
     const int tiles = (n_rows + kWdBT - 1) / kWdBT + min(a.E, n_rows);
-    const dim3 grid((a.N + kWdRows - 1) / kWdRows, tiles);
+    const dim3 grid((groups + kWdGroups - 1) / kWdGroups, tiles);
     switch (epi) {
       case EPI_SWIGLU: hipLaunchKernelGGL((ffn_wide_kernel<EPI_SWIGLU, false>), grid, dim3(256), 0, s, a); break;
       case EPI_COMBINE: hipLaunchKernelGGL((ffn_wide_kernel<EPI_COMBINE, true>), grid, dim3(256), 0, s, a); break;

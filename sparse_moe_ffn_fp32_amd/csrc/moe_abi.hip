@@ -21,7 +21,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t ids, w, counts, offsets, sorted, h, total;
+  size_t ids, w, counts, offsets, sorted, scratch, h, total;
 };
 
 bool sizes_ok(int T, int E, int k) {
@@ -38,6 +38,7 @@ WsLayout layout(int T, int E, int k) {
   l.counts = off;   off = align_up(off + (size_t)E * 4);
   l.offsets = off;  off = align_up(off + (size_t)(E + 1) * 4);
   l.sorted = off;   off = align_up(off + n * 4);
+  l.scratch = off;  off = align_up(off + moe::route_scratch_bytes(T, E));
   l.h = off;        off = align_up(off + n * (size_t)moe::kI * 2);
   l.total = off;
   return l;
@@ -88,7 +89,8 @@ moe_status_t after_launch(hipError_t err, hipStream_t s) {
 moe_status_t check_weights(const uint8_t* w13c, const uint8_t* w13s, const uint16_t* b13,
                            const uint8_t* w2c, const uint8_t* w2s, const uint16_t* b2) {
   if (!w13c || !w13s || !b13 || !w2c || !w2s || !b2) return MOE_ERROR_INVALID_VALUE;
-  if (!aligned(w13c, 16) || !aligned(w2c, 16) || !aligned(b13, 2) || !aligned(b2, 2))
+  if (!aligned(w13c, 16) || !aligned(w2c, 16) || !aligned(w13s, 4) || !aligned(w2s, 4) ||
+      !aligned(b13, 8) || !aligned(b2, 8))
     return MOE_ERROR_MISALIGNED;
   return MOE_SUCCESS;
 }
@@ -139,16 +141,32 @@ const char* moe_status_string(moe_status_t status) {
 }
 
 moe_status_t moe_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
-                       int32_t* topk_ids, float* topk_w, float* logits, void* stream) {
+                       int32_t* topk_ids, float* topk_w, float* logits, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
   if (T == 0) return MOE_SUCCESS;
   if (!x || !Wr || !br || !topk_ids || !topk_w) return MOE_ERROR_INVALID_VALUE;
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(br, 4) || !aligned(topk_ids, 4) ||
       !aligned(topk_w, 4) || !aligned(logits, 4))
     return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(moe::launch_route(x, Wr, br, T, E, k, topk_ids, topk_w, logits, nullptr, s), s);
+  float* scratch = reinterpret_cast<float*>(static_cast<char*>(ws) + layout(T, E, k).scratch);
+  return after_launch(moe::launch_route(x, Wr, br, T, E, k, topk_ids, topk_w, logits, nullptr,
+                                        scratch, nullptr, nullptr, nullptr, s), s);
+}
+
+moe_status_t moe_pack_weights(const uint8_t* codes, const uint8_t* scales, int E, int N,
+                              uint8_t* packed_codes, uint8_t* packed_scales, void* stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || N < 64 || N > 65536 || N % 64 != 0)
+    return MOE_ERROR_INVALID_VALUE;
+  if (!codes || !scales || !packed_codes || !packed_scales) return MOE_ERROR_INVALID_VALUE;
+  if (!aligned(codes, 16) || !aligned(packed_codes, 16) || !aligned(packed_scales, 4))
+    return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(moe::launch_pack(codes, scales, E, N, packed_codes, packed_scales, s), s);
 }
 
 moe_status_t moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* counts,
@@ -189,6 +207,43 @@ moe_status_t moe_expert_ffn(const uint16_t* x, const int32_t* offsets, const int
   return after_launch(moe::launch_ffn(a2, moe::EPI_STORE_Y, n, s), s);
 }
 
+moe_status_t moe_gate_up(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_rows,
+                         const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
+                         int T, int E, int k, uint16_t* h, void* stream) {
+  if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !offsets || !sorted_rows || !w13_codes || !w13_scales || !b13 || !h)
+    return MOE_ERROR_INVALID_VALUE;
+  if (!aligned(x, 16) || !aligned(h, 16) || !aligned(w13_codes, 16) || !aligned(w13_scales, 4) ||
+      !aligned(b13, 8) || !aligned(offsets, 4) || !aligned(sorted_rows, 4))
+    return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FfnArgs a = ffn_args(x, offsets, sorted_rows, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
+  a.h_out = h;
+  return after_launch(moe::launch_ffn(a, moe::EPI_SWIGLU, T * k, s), s);
+}
+
+moe_status_t moe_down_accumulate(const uint16_t* h, const int32_t* offsets,
+                                 const int32_t* sorted_rows, const float* topk_w,
+                                 const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                 const uint16_t* b2, int T, int E, int k, float* out,
+                                 void* stream) {
+  if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!h || !offsets || !sorted_rows || !topk_w || !w2_codes || !w2_scales || !b2 || !out)
+    return MOE_ERROR_INVALID_VALUE;
+  if (!aligned(h, 16) || !aligned(out, 16) || !aligned(w2_codes, 16) || !aligned(w2_scales, 4) ||
+      !aligned(b2, 8) || !aligned(offsets, 4) || !aligned(sorted_rows, 4) || !aligned(topk_w, 4))
+    return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FfnArgs a = ffn_args(h, offsets, sorted_rows, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
+  a.topk_w = topk_w;
+  a.out = out;
+  return after_launch(moe::launch_ffn(a, moe::EPI_COMBINE, T * k, s), s);
+}
+
 moe_status_t moe_combine(const float* y, const float* topk_w, int T, int k, float* out,
                          void* stream) {
   if (T < 0 || k < 1 || k > MOE_MAX_TOPK || (long long)T * k > MOE_MAX_ROUTED)
@@ -221,11 +276,13 @@ moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
   int32_t* counts = reinterpret_cast<int32_t*>(base + l.counts);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + l.offsets);
   int32_t* sorted = reinterpret_cast<int32_t*>(base + l.sorted);
+  float* scratch = reinterpret_cast<float*>(base + l.scratch);
   uint16_t* h = reinterpret_cast<uint16_t*>(base + l.h);
   const int n = T * k;
-  // router + top-k + softmax; also clears `out` for the accumulating epilogue
-  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, out, s), s));
-  MOE_TRY(after_launch(moe::launch_permute(ids, n, E, counts, offsets, sorted, s), s));
+  // router + top-k + softmax + expert permutation; also clears `out` for the
+  // accumulating down-projection epilogue
+  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, out, scratch, counts,
+                                         offsets, sorted, s), s));
   FfnArgs a13 = ffn_args(x, offsets, sorted, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
   a13.h_out = h;
   MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));

@@ -17,6 +17,16 @@ constexpr float kSwigluLimit = 7.0f;    // swiglu_limit, raw config.json fields
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 8;
 
+// Packed MXFP4 order (moe_pack_weights): per 64-row group, K steps of four MX
+// blocks; step s holds four 16-row tiles of 64 lanes x 16 code bytes (the
+// last step, blocks 88 and 89, only lanes 0..31), then scales as 4 bytes per
+// lane (one per tile).
+constexpr int kSteps = 23;               // ceil(90 / 4)
+constexpr int kFullSteps = 22;           // steps with all four blocks
+constexpr int kStepCodeBytes = 4096;     // four tiles x 1 KiB
+constexpr int kGroupCodeBytes = 64 * kRowCodeBytes;    // 92,160
+constexpr int kGroupScaleBytes = 64 * kRowScaleBytes;  // 5,760
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -29,8 +29,17 @@ struct FfnArgs {
   int gather;                   // 1: activation row = sorted_rows[p] / k, 0: row p
 };
 
+// Router + top-k + softmax. `zero_out` (optional) is cleared for the
+// accumulating down projection; with `counts` non-null the expert permutation
+// is built as well. `scratch` holds route_scratch_bytes(T, E) bytes.
 hipError_t launch_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
-                        int32_t* ids, float* w, float* logits, float* zero_out, hipStream_t s);
+                        int32_t* ids, float* w, float* logits, float* zero_out, float* scratch,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_rows, hipStream_t s);
+size_t route_scratch_bytes(int T, int E);
+
+// canonical MXFP4 codes/scales [E, N, ...] -> the packed order of the GEMMs
+hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, int E, int N, uint8_t* pcodes,
+                       uint8_t* pscales, hipStream_t s);
 
 hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_rows, hipStream_t s);

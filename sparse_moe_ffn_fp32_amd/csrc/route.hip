@@ -1,4 +1,4 @@
-// Router GEMM + in-register top-k + softmax over the selected logits.
+// Router GEMM + top-k + softmax over the selected logits.
 //
 // logits[t, e] = sum_h x[t, h] Wr[e, h] + br[e]  (gpt-oss-120b techniques map,
 // "Checked in its code" table, row "Auxiliary-loss-free load balancing": the
@@ -7,14 +7,36 @@
 //
 // fp32 router on bf16 matrix cores: x is bf16, and each fp32 weight is split
 // exactly into three bf16 pieces (hi + mid + lo, 8 significant bits each).
-// Every product x * piece is exact in fp32, and the matrix core accumulates in
+// Every product x * piece is exact in fp32 and the matrix core accumulates in
 // fp32, so the result is an fp32-accumulated dot product of the fp32 weights.
-// Block = 32 tokens; its waves split K and their partial sums are added in a
-// fixed wave order through LDS (deterministic).
+// A wave computes a 32-token x 32*MT-expert tile of 32x32x16 MFMAs over a K
+// range, with a register prefetch ring over its K steps.
+//
+// Two schedules, chosen by T (both deterministic, fixed summation order):
+//  * few tokens (T <= 128, T*E <= 4096): the K dimension is cut into 20 chunks, one wave
+//    per (32-token tile, chunk) writes partial logits to scratch; a single
+//    1024-thread block adds the 20 partials in chunk order, adds the bias,
+//    selects the top k and, for the full layer, also builds the expert
+//    permutation (so decoding needs two small launches for all routing).
+//  * many tokens: a block per 32 tokens, its waves split K and add their
+//    partial tiles in wave order through LDS, then select the top k.
+#include "moe_block_permute.h"
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace moe {
+
+constexpr int kRouteChunks = 20;                  // K chunks of the few-token schedule
+constexpr int kRouteChunkSteps = kH / 16 / kRouteChunks;  // 9 MFMA steps of 16 K
+constexpr int kRouteSmallT = 128;
+constexpr int kRouteMaxPairs = 4 * 1024;   // T * E of the few-token schedule (LDS logits)
+static_assert(kRouteChunkSteps * 16 * kRouteChunks == kH, "chunks must tile K");
+
+static bool few_tokens(int T, int E) { return T <= kRouteSmallT && T * E <= kRouteMaxPairs; }
+
+size_t route_scratch_bytes(int T, int E) {
+  return few_tokens(T, E) ? (size_t)kRouteChunks * T * E * sizeof(float) : 0;
+}
 
 __device__ __forceinline__ void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   const uint32_t u = __float_as_uint(v);
@@ -43,16 +65,188 @@ __device__ __forceinline__ void split_frag(const float4& a, const float4& b, bf1
   fl = u4_as_bf16x8(pl);
 }
 
-struct Cand {
-  float v;
-  int id;
+template <int MT>
+struct RStage {
+  uint4 xv;
+  float4 w[MT][2];
 };
+
+// Operand loader of one wave: tokens tok0 + (lane & 31), experts 32mt +
+// (lane & 31), K from k0 in steps of 16 (lane half hh takes 8 of them).
+template <int MT>
+struct RouteLoader {
+  const uint16_t* xrow;
+  bool tok_ok;
+  const float* wrow[MT];
+  bool e_ok[MT];
+
+  __device__ __forceinline__ void init(const uint16_t* x, const float* Wr, int T, int E, int tok,
+                                       int k0, int lane) {
+    // padded tokens / experts read a clamped valid row: their results are
+    // never used, and the loads stay unconditional
+    const int n = lane & 31;
+    const int hh = lane >> 5;
+    tok_ok = tok < T;
+    xrow = x + (size_t)min(tok, T - 1) * kH + k0 + 8 * hh;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int e = mt * 32 + n;
+      e_ok[mt] = e < E;
+      wrow[mt] = Wr + (size_t)min(e, E - 1) * kH + k0 + 8 * hh;
+    }
+  }
+  __device__ __forceinline__ void load(RStage<MT>& st, int s) const {
+    st.xv = *reinterpret_cast<const uint4*>(xrow + 16 * s);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      st.w[mt][0] = *reinterpret_cast<const float4*>(wrow[mt] + 16 * s);
+      st.w[mt][1] = *reinterpret_cast<const float4*>(wrow[mt] + 16 * s + 4);
+    }
+  }
+};
+
+template <int MT>
+__device__ __forceinline__ void route_mma(const RStage<MT>& st, f32x16 (&acc)[MT]) {
+  const bf16x8 xb = u4_as_bf16x8(st.xv);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    bf16x8 fh, fm, fl;
+    split_frag(st.w[mt][0], st.w[mt][1], fh, fm, fl);
+    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl, xb, acc[mt], 0, 0, 0);
+    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fm, xb, acc[mt], 0, 0, 0);
+    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh, xb, acc[mt], 0, 0, 0);
+  }
+}
+
+template <int MT>
+constexpr int route_depth() {
+  return MT <= 1 ? 8 : MT <= 2 ? 6 : MT <= 4 ? 4 : 2;
+}
+
+// K loop over NSTEPS steps with a register prefetch ring: fully unrolled for
+// short K ranges (exact load counting), a rolled ring otherwise (the long
+// unroll would spill).
+template <int MT, int NSTEPS>
+__device__ __forceinline__ void route_kloop(const RouteLoader<MT>& L, f32x16 (&acc)[MT]) {
+  constexpr int D = route_depth<MT>() < NSTEPS ? route_depth<MT>() : NSTEPS;
+  RStage<MT> st[D];
+#pragma unroll
+  for (int q = 0; q < D; ++q) L.load(st[q], q);
+  if constexpr (NSTEPS <= 16) {
+#pragma unroll
+    for (int s = 0; s < NSTEPS; ++s) {
+      route_mma<MT>(st[s % D], acc);
+      if (s + D < NSTEPS) L.load(st[s % D], s + D);
+    }
+  } else {
+    for (int s0 = 0; s0 < NSTEPS; s0 += D) {
+#pragma unroll
+      for (int q = 0; q < D; ++q) {
+        const int s = s0 + q;
+        if (s < NSTEPS) {
+          route_mma<MT>(st[q], acc);
+          if (s + D < NSTEPS) L.load(st[q], s + D);
+        }
+      }
+    }
+  }
+}
 
 __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
-// MT = ceil(E / 32) expert tiles, WK = waves splitting K.
+// Insert (cv, ci) into the descending list (bv, bi) of length k <= KM; branch-free.
+template <int KM>
+__device__ __forceinline__ void topk_insert(float (&bv)[KM], int (&bi)[KM], int k, float cv, int ci) {
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    if (j < k) {
+      const bool b = better(cv, ci, bv[j], bi[j]);
+      const float tv = b ? bv[j] : cv;
+      const int ti = b ? bi[j] : ci;
+      bv[j] = b ? cv : bv[j];
+      bi[j] = b ? ci : bi[j];
+      cv = tv;
+      ci = ti;
+    }
+  }
+}
+
+// Top-k (descending, ties -> lower expert id) and softmax over the selected
+// logits of one token, by LPT consecutive lanes: lane `sub` scans experts
+// sub, sub + LPT, ... (logit of expert e at lg[e * e_stride]), then the lanes
+// merge their lists in log2(LPT) butterfly steps. All lanes of the wave must
+// call it. When `active`, lanes sub < k write slot sub of ids_t / w_t (and
+// lds_ids_t if non-null).
+template <int LPT, int KM>
+__device__ __forceinline__ void lanes_topk_km(const float* lg, int e_stride, int E, int k,
+                                              bool active, int32_t* ids_t, float* w_t,
+                                              int32_t* lds_ids_t) {
+  const int sub = threadIdx.x & (LPT - 1);
+  float bv[KM];
+  int bi[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    bv[j] = -INFINITY;
+    bi[j] = 0x7FFFFFFF;
+  }
+  if (active)
+    for (int e = sub; e < E; e += LPT) topk_insert<KM>(bv, bi, k, lg[e * e_stride], e);
+#pragma unroll
+  for (int d = 1; d < LPT; d <<= 1) {
+    float pv[KM];
+    int pi[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      pv[j] = __shfl_xor(bv[j], d, 64);
+      pi[j] = __shfl_xor(bi[j], d, 64);
+    }
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) topk_insert<KM>(bv, bi, k, pv[j], pi[j]);
+  }
+  if (!active) return;
+  float ex[KM];
+  float z = 0.f;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    ex[j] = (j < k) ? __expf(bv[j] - bv[0]) : 0.f;
+    z += ex[j];
+  }
+  const float inv = 1.0f / z;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    if (j < k && sub == j) {
+      ids_t[j] = bi[j];
+      w_t[j] = ex[j] * inv;
+      if (lds_ids_t) lds_ids_t[j] = bi[j];
+    }
+  }
+}
+
+template <int LPT>
+__device__ __forceinline__ void lanes_topk(const float* lg, int e_stride, int E, int k, bool active,
+                                           int32_t* ids_t, float* w_t, int32_t* lds_ids_t) {
+  if (k == 1) lanes_topk_km<LPT, 1>(lg, e_stride, E, k, active, ids_t, w_t, lds_ids_t);
+  else if (k == 2) lanes_topk_km<LPT, 2>(lg, e_stride, E, k, active, ids_t, w_t, lds_ids_t);
+  else if (k <= 4) lanes_topk_km<LPT, 4>(lg, e_stride, E, k, active, ids_t, w_t, lds_ids_t);
+  else lanes_topk_km<LPT, 8>(lg, e_stride, E, k, active, ids_t, w_t, lds_ids_t);
+}
+
+constexpr int kTopkLanes = 8;   // lanes per token in the top-k
+
+__device__ __forceinline__ void zero_rows_slice(float* out, int T, int part, int parts, int tid,
+                                                int nthreads) {
+  const long long total4 = (long long)T * (kH / 4);
+  const long long per = (total4 + parts - 1) / parts;
+  const long long b = (long long)part * per;
+  const long long end = min(total4, b + per);
+  float4* o = reinterpret_cast<float4*>(out);
+  for (long long i = b + tid; i < end; i += nthreads) o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// ---------------------------------------------------------------- many tokens
 template <int MT, int WK>
 __global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restrict__ x,
                                                         const float* __restrict__ Wr,
@@ -62,7 +256,7 @@ __global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restri
                                                         float* __restrict__ logits,
                                                         float* __restrict__ zero_out) {
   constexpr int KW = kH / WK;      // K range of one wave
-  constexpr int KSTEPS = KW / 16;  // 16-deep MFMA steps per wave
+  constexpr int KSTEPS = KW / 16;  // MFMA steps of one wave
   constexpr int LDR = 33;          // padded row of the reduction buffer
   static_assert(KW % 16 == 0, "K split must be a multiple of 16");
   extern __shared__ float red[];   // [MT * 32][LDR]
@@ -72,46 +266,16 @@ __global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restri
   const int tok0 = blockIdx.x * 32;
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int tok = tok0 + n;
-  const bool tok_ok = tok < T;
 
   f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
-
-  const uint16_t* xrow = x + (size_t)(tok_ok ? tok : 0) * kH + wave * KW + 8 * hh;
-  const float* wrow[MT];
-  bool e_ok[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int e = mt * 32 + n;
-    e_ok[mt] = e < E;
-    wrow[mt] = Wr + (size_t)(e_ok[mt] ? e : 0) * kH + wave * KW + 8 * hh;
-  }
-
-#pragma unroll 3
-  for (int s = 0; s < KSTEPS; ++s) {
-    uint4 xv = make_uint4(0, 0, 0, 0);
-    if (tok_ok) xv = *reinterpret_cast<const uint4*>(xrow + 16 * s);
-    const bf16x8 xb = u4_as_bf16x8(xv);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      if (e_ok[mt]) {
-        a = *reinterpret_cast<const float4*>(wrow[mt] + 16 * s);
-        b = *reinterpret_cast<const float4*>(wrow[mt] + 16 * s + 4);
-      }
-      bf16x8 fh, fm, fl;
-      split_frag(a, b, fh, fm, fl);
-      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl, xb, acc[mt], 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fm, xb, acc[mt], 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh, xb, acc[mt], 0, 0, 0);
-    }
-  }
+  RouteLoader<MT> L;
+  L.init(x, Wr, T, E, tok0 + n, wave * KW, lane);
+  route_kloop<MT, KSTEPS>(L, acc);
 
   // Fixed-order split-K reduction: red[e][token] = sum over waves 0..WK-1.
-  // Result layout of the 32x32 tile: lane holds column n (token) and rows
-  // 8q + 4*hh + j (experts) in element 4q + j.
+  // 32x32 result layout: lane holds column n (token), rows 8q + 4hh + j.
   for (int w = 0; w < WK; ++w) {
     if (wave == w) {
 #pragma unroll
@@ -120,118 +284,203 @@ __global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restri
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int m = mt * 32 + 8 * q + 4 * hh + j;
-            float* p = &red[m * LDR + n];
+            float* p = &red[(mt * 32 + 8 * q + 4 * hh + j) * LDR + n];
             *p = (w == 0) ? acc[mt][4 * q + j] : (*p + acc[mt][4 * q + j]);
           }
     }
     __syncthreads();
   }
 
-  // Top-k, one wave per token: lane holds experts lane + 64q.
-  for (int tt = wave; tt < 32; tt += WK) {
+  // bias, optional logits output
+  for (int i = threadIdx.x; i < 32 * E; i += WK * 64) {
+    const int e = i / 32, tt = i % 32;
+    const float v = red[e * LDR + tt] + br[e];
+    red[e * LDR + tt] = v;
+    if (logits && tok0 + tt < T) logits[(size_t)(tok0 + tt) * E + e] = v;
+  }
+  __syncthreads();
+  // top-k: 8 lanes per token, the first 256 threads cover the 32 tokens
+  if (threadIdx.x < 32 * kTopkLanes) {
+    const int tt = threadIdx.x / kTopkLanes;
     const int t = tok0 + tt;
-    if (t >= T) break;
-    float v[4];
-    int id[4];
+    lanes_topk<kTopkLanes>(red + tt, LDR, E, k, t < T, ids + (size_t)t * k, wts + (size_t)t * k,
+                           nullptr);
+  }
+  if (zero_out) zero_rows_slice(zero_out, T, blockIdx.x, gridDim.x, threadIdx.x, WK * 64);
+}
+
+// ---------------------------------------------------------------- few tokens
+template <int MT>
+__global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ Wr, int T,
+                                                           int E, float* __restrict__ partial,
+                                                           float* __restrict__ zero_out) {
+  const int lane = threadIdx.x;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int tok = blockIdx.x * 32 + n;
+  const int kc = blockIdx.y;
+  f32x16 acc[MT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      if (e < E) {
-        v[q] = red[e * LDR + tt] + br[e];
-        id[q] = e;
-        if (logits) logits[(size_t)t * E + e] = v[q];
-      } else {
-        v[q] = -INFINITY;
-        id[q] = 0x7FFFFFFF;
-      }
-    }
-    float sel_v[kMaxTopK];
-    int sel_i[kMaxTopK];
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+  RouteLoader<MT> L;
+  L.init(x, Wr, T, E, tok, kc * kRouteChunkSteps * 16, lane);
+  route_kloop<MT, kRouteChunkSteps>(L, acc);
+  if (tok < T) {
+    float* prow = partial + ((size_t)kc * T + tok) * E;
 #pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-      if (r < k) {
-        float bv = v[0];
-        int bi = id[0];
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int q = 1; q < 4; ++q)
-          if (better(v[q], id[q], bv, bi)) { bv = v[q]; bi = id[q]; }
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-          const float ov = __shfl_xor(bv, d, 64);
-          const int oi = __shfl_xor(bi, d, 64);
-          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        for (int j = 0; j < 4; ++j) {
+          const int e = mt * 32 + 8 * q + 4 * hh + j;
+          if (e < E) prow[e] = acc[mt][4 * q + j];
         }
-        sel_v[r] = bv;
-        sel_i[r] = bi;
+  }
+  if (zero_out)
+    zero_rows_slice(zero_out, T, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y, lane, 64);
+}
+
+// One 1024-thread block: logits = bias + sum of the chunk partials in chunk
+// order (one thread per (token, expert) pair, all partial loads in flight at
+// once), then one wave per token selects the top k from LDS; with PERMUTE the
+// block also builds the expert permutation of the T*k slots.
+template <bool PERMUTE, int PAIRS>
+__global__ __launch_bounds__(kPermThreads) void route_finish_kernel(
+    const float* __restrict__ partial, const float* __restrict__ br, int T, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows) {
+  __shared__ PermuteSmem sm;
+  __shared__ int lds_ids[kRouteSmallT * kMaxTopK];
+  __shared__ float lg[kRouteMaxPairs + kMaxExperts];   // [E][T + 1]
+  __shared__ float sel_v[kRouteSmallT * kMaxTopK];
+  const int tid = threadIdx.x;
+  const int TE = T * E;
+  const int ldt = T + 1;   // padded expert-major stride: a token's lanes hit distinct banks
+  float bias[PAIRS];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (id[q] == bi) { v[q] = -INFINITY; id[q] = 0x7FFFFFFF; }
-      }
+  for (int j = 0; j < PAIRS; ++j) bias[j] = br[min(tid + j * kPermThreads, TE - 1) % E];
+  float acc[PAIRS];
+#pragma unroll
+  for (int j = 0; j < PAIRS; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int c = 0; c < kRouteChunks; ++c) {
+#pragma unroll
+    for (int j = 0; j < PAIRS; ++j) {
+      const int i = min(tid + j * kPermThreads, TE - 1);
+      acc[j] += partial[(size_t)c * TE + i];
     }
-    // softmax over the k selected logits (sel_v[0] is the largest)
-    float z = 0.f;
-    float ex[kMaxTopK];
+  }
 #pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-      ex[r] = (r < k) ? __expf(sel_v[r] - sel_v[0]) : 0.f;
-      z += ex[r];
+  for (int j = 0; j < PAIRS; ++j) {
+    const int i = tid + j * kPermThreads;
+    if (i < TE) {
+      const int t = i / E, e = i - (i / E) * E;
+      const float v = acc[j] + bias[j];
+      lg[e * ldt + t] = v;
+      if (logits) logits[i] = v;
     }
-    const float inv = 1.0f / z;
+  }
+  __syncthreads();
+  // Top-k by rank: the thread of (token t, expert e) counts the experts that
+  // beat e (larger logit, or equal logit and lower id); e is selected at
+  // position `rank` when rank < k. No cross-lane traffic; the logits of a
+  // token are LDS broadcasts.
 #pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-      if (r < k && lane == r) {
-        ids[(size_t)t * k + r] = sel_i[r];
-        wts[(size_t)t * k + r] = ex[r] * inv;
+  for (int j = 0; j < PAIRS; ++j) {
+    const int i = tid + j * kPermThreads;
+    if (i < TE) {
+      const int t = i / E, e = i - (i / E) * E;
+      const float v = lg[e * ldt + t];
+      int rank = 0;
+      for (int e2 = 0; e2 < E; ++e2) rank += better(lg[e2 * ldt + t], e2, v, e) ? 1 : 0;
+      if (rank < k) {
+        sel_v[t * k + rank] = v;
+        lds_ids[t * k + rank] = e;
       }
     }
   }
-
-  // Optionally clear this block's rows of the layer output (the fused down
-  // projection accumulates into it).
-  if (zero_out) {
-    const int rows = min(32, T - tok0);
-    float4* o = reinterpret_cast<float4*>(zero_out + (size_t)tok0 * kH);
-    const int n4 = rows * (kH / 4);
-    for (int i = threadIdx.x; i < n4; i += WK * 64) o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();
+  // softmax over the selected logits (position 0 holds the largest)
+  for (int i = tid; i < T * k; i += kPermThreads) {
+    const int t = i / k;
+    const float m = sel_v[t * k];
+    float z = 0.f;
+    for (int j = 0; j < k; ++j) z += __expf(sel_v[t * k + j] - m);
+    ids[i] = lds_ids[i];
+    wts[i] = __expf(sel_v[i] - m) / z;
+  }
+  if constexpr (PERMUTE) {
+    __syncthreads();
+    block_permute(lds_ids, T * k, E, counts, offsets, sorted_rows, sm);
   }
 }
 
-template <int MT, int WK>
-static hipError_t launch_route_t(const uint16_t* x, const float* Wr, const float* br, int T, int E,
-                                 int k, int32_t* ids, float* w, float* logits, float* zero_out,
-                                 hipStream_t s) {
+template <bool PERMUTE>
+static void launch_finish(const float* scratch, const float* br, int T, int E, int k, int32_t* ids,
+                          float* w, float* logits, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_rows, hipStream_t s) {
+  const int pairs = (T * E + kPermThreads - 1) / kPermThreads;
+#define MOE_FINISH(P)                                                                             \
+  hipLaunchKernelGGL((route_finish_kernel<PERMUTE, P>), dim3(1), dim3(kPermThreads), 0, s, scratch, \
+                     br, T, E, k, ids, w, logits, counts, offsets, sorted_rows)
+  if (pairs <= 1) MOE_FINISH(1);
+  else if (pairs <= 2) MOE_FINISH(2);
+  else MOE_FINISH(4);
+#undef MOE_FINISH
+}
+
+// ---------------------------------------------------------------- launch
+template <int MT>
+static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const float* br, int T, int E,
+                                  int k, int32_t* ids, float* w, float* logits, float* zero_out,
+                                  float* scratch, int32_t* counts, int32_t* offsets,
+                                  int32_t* sorted_rows, hipStream_t s) {
+  if (few_tokens(T, E)) {
+    const dim3 grid((T + 31) / 32, kRouteChunks);
+    hipLaunchKernelGGL((route_partial_kernel<MT>), grid, dim3(64), 0, s, x, Wr, T, E, scratch, zero_out);
+    if (counts)
+      launch_finish<true>(scratch, br, T, E, k, ids, w, logits, counts, offsets, sorted_rows, s);
+    else
+      launch_finish<false>(scratch, br, T, E, k, ids, w, logits, counts, offsets, sorted_rows, s);
+    return hipGetLastError();
+  }
   const int blocks = (T + 31) / 32;
   const size_t lds = (size_t)MT * 32 * 33 * sizeof(float);
-  hipLaunchKernelGGL((route_kernel<MT, WK>), dim3(blocks), dim3(WK * 64), lds, s, x, Wr, br, T, E,
-                     k, ids, w, logits, zero_out);
-  return hipGetLastError();
+  // 12 waves split K when few blocks would run; only for one expert tile,
+  // where the 768-thread register budget holds the prefetch ring.
+  if constexpr (MT == 1) {
+    if (blocks < 256) {
+      hipLaunchKernelGGL((route_kernel<1, 12>), dim3(blocks), dim3(12 * 64), lds, s, x, Wr, br, T, E,
+                         k, ids, w, logits, zero_out);
+    } else {
+      hipLaunchKernelGGL((route_kernel<1, 4>), dim3(blocks), dim3(4 * 64), lds, s, x, Wr, br, T, E,
+                         k, ids, w, logits, zero_out);
+    }
+  } else {
+    hipLaunchKernelGGL((route_kernel<MT, 4>), dim3(blocks), dim3(4 * 64), lds, s, x, Wr, br, T, E, k,
+                       ids, w, logits, zero_out);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !counts) return err;
+  return launch_permute(ids, T * k, E, counts, offsets, sorted_rows, s);
 }
 
 hipError_t launch_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
-                        int32_t* ids, float* w, float* logits, float* zero_out, hipStream_t s) {
-  const int mt = (E + 31) / 32;
-  const int blocks = (T + 31) / 32;
-  // Few token blocks: split K over 12 waves to spread the work; many: 4 waves.
-  const bool wide = blocks < 256 && mt <= 4;
-#define MOE_ROUTE_CASE(M)                                                                   \
-  case M:                                                                                   \
-    return wide ? launch_route_t<(M <= 4 ? M : 4), 12>(x, Wr, br, T, E, k, ids, w, logits, \
-                                                       zero_out, s)                         \
-                : launch_route_t<M, 4>(x, Wr, br, T, E, k, ids, w, logits, zero_out, s);
-  switch (mt) {
-    MOE_ROUTE_CASE(1)
-    MOE_ROUTE_CASE(2)
-    MOE_ROUTE_CASE(3)
-    MOE_ROUTE_CASE(4)
-    MOE_ROUTE_CASE(5)
-    MOE_ROUTE_CASE(6)
-    MOE_ROUTE_CASE(7)
-    MOE_ROUTE_CASE(8)
-    default:
-      return hipErrorInvalidValue;
+                        int32_t* ids, float* w, float* logits, float* zero_out, float* scratch,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_rows, hipStream_t s) {
+  switch ((E + 31) / 32) {
+    case 1: return launch_route_mt<1>(x, Wr, br, T, E, k, ids, w, logits, zero_out, scratch, counts, offsets, sorted_rows, s);
+    case 2: return launch_route_mt<2>(x, Wr, br, T, E, k, ids, w, logits, zero_out, scratch, counts, offsets, sorted_rows, s);
+    case 3: return launch_route_mt<3>(x, Wr, br, T, E, k, ids, w, logits, zero_out, scratch, counts, offsets, sorted_rows, s);
+    case 4: return launch_route_mt<4>(x, Wr, br, T, E, k, ids, w, logits, zero_out, scratch, counts, offsets, sorted_rows, s);
+    case 5: return launch_route_mt<5>(x, Wr, br, T, E, k, ids, w, logits, zero_out, scratch, counts, offsets, sorted_rows, s);
+    case 6: return launch_route_mt<6>(x, Wr, br, T, E, k, ids, w, logits, zero_out, scratch, counts, offsets, sorted_rows, s);
+    case 7: return launch_route_mt<7>(x, Wr, br, T, E, k, ids, w, logits, zero_out, scratch, counts, offsets, sorted_rows, s);
+    case 8: return launch_route_mt<8>(x, Wr, br, T, E, k, ids, w, logits, zero_out, scratch, counts, offsets, sorted_rows, s);
+    default: return hipErrorInvalidValue;
   }
-#undef MOE_ROUTE_CASE
 }
 
 }  // namespace moe

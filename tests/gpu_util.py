@@ -16,17 +16,46 @@ MEAN_REL_L2 = 5e-3
 NEAR_TIE_GAP = 1e-4
 
 
-def to_device(inp, device="cuda"):
+def to_device(inp, device="cuda", pack=True):
+    """Host arrays -> device tensors; with `pack`, the expert weights are also
+    packed on the GPU (keys p13c, p13s, p2c, p2s)."""
+    import sparse_moe_ffn_fp32_amd as moe
     d = {}
     for key, a in inp.items():
         if a.dtype == np.uint16:
             a = a.view(np.int16)
         d[key] = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    if pack and "w13_codes" in d:
+        d["p13c"], d["p13s"], d["p2c"], d["p2s"] = moe.pack_expert_weights(
+            d["w13_codes"], d["w13_scales"], d["w2_codes"], d["w2_scales"])
     return d
 
 
 def weights_args(d):
-    return (d["w13_codes"], d["w13_scales"], d["b13"], d["w2_codes"], d["w2_scales"], d["b2"])
+    """Packed expert weights in the argument order of the layer calls."""
+    return (d["p13c"], d["p13s"], d["b13"], d["p2c"], d["p2s"], d["b2"])
+
+
+def pack_reference(codes: np.ndarray, scales: np.ndarray):
+    """The documented packed order, written independently of the library:
+    offset(codes) = G*92160 + s*4096 + m*(s < 22 ? 1024 : 512) + l*16,
+    offset(scales) = G*5760 + s*256 + l*4 + m, for row 64G + 16m + r,
+    MX block 4s + g, lane l = 16g + r."""
+    E, N, _ = codes.shape
+    pc = np.zeros(E * N * 1440, dtype=np.uint8)
+    ps = np.zeros(E * N * 90, dtype=np.uint8)
+    rows = np.arange(E * N)
+    G, rin = rows // 64, rows % 64
+    m, r = rin // 16, rin % 16
+    cflat = codes.reshape(E * N, 90, 16)
+    sflat = scales.reshape(E * N, 90)
+    for kb in range(90):
+        s, g = kb // 4, kb % 4
+        l = 16 * g + r
+        off = G * 92160 + s * 4096 + m * (1024 if s < 22 else 512) + l * 16
+        pc[off[:, None] + np.arange(16)[None, :]] = cflat[:, kb, :]
+        ps[G * 5760 + s * 256 + l * 4 + m] = sflat[:, kb]
+    return pc.reshape(codes.shape), ps.reshape(scales.shape)
 
 
 def out_metrics(got: np.ndarray, ref: np.ndarray):

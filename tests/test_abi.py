@@ -55,8 +55,10 @@ def test_workspace_size(L):
     assert L.moe_workspace_size(64, 32, 8) > L.moe_workspace_size(64, 32, 4)
 
 
-def route(L, T=4, E=32, k=4, x=A, Wr=A, br=A, ids=A, w=A, logits=None):
-    return L.moe_route(P(x), P(Wr), P(br), T, E, k, P(ids), P(w), P(logits), None)
+def route(L, T=4, E=32, k=4, x=A, Wr=A, br=A, ids=A, w=A, logits=None, ws=A, nbytes=None):
+    if nbytes is None:
+        nbytes = L.moe_workspace_size(max(T, 0), E, k)
+    return L.moe_route(P(x), P(Wr), P(br), T, E, k, P(ids), P(w), P(logits), P(ws), nbytes, None)
 
 
 def test_route_validation(L):
@@ -73,6 +75,21 @@ def test_route_validation(L):
     assert route(L, Wr=A + 4) == MISALIGNED
     assert route(L, ids=A + 2) == MISALIGNED
     assert route(L, logits=A + 1) == MISALIGNED
+    assert route(L, ws=None) == WORKSPACE
+    assert route(L, nbytes=64) == WORKSPACE
+
+
+def test_pack_validation(L):
+    pk = lambda E=2, N=64, c=A, s=A, pc=A, ps=A: L.moe_pack_weights(P(c), P(s), E, N, P(pc), P(ps), None)
+    assert pk(E=0) == INVALID
+    assert pk(E=257) == INVALID
+    assert pk(N=32) == INVALID
+    assert pk(N=100) == INVALID
+    assert pk(c=None) == INVALID
+    assert pk(ps=None) == INVALID
+    assert pk(c=A + 8) == MISALIGNED
+    assert pk(pc=A + 4) == MISALIGNED
+    assert pk(ps=A + 2) == MISALIGNED
 
 
 def permute(L, T=4, E=32, k=4, ids=A, counts=A, offsets=A, rows=A, ws=A, nbytes=None):
@@ -107,8 +124,10 @@ def test_expert_ffn_validation(L):
     assert ffn(L, b2=None) == INVALID
     assert ffn(L, y=None) == INVALID
     assert ffn(L, c13=A + 8) == MISALIGNED
+    assert ffn(L, s13=A + 2) == MISALIGNED
     assert ffn(L, c2=A + 1) == MISALIGNED
     assert ffn(L, b13=A + 1) == MISALIGNED
+    assert ffn(L, b2=A + 4) == MISALIGNED
     assert ffn(L, y=A + 4) == MISALIGNED
     assert ffn(L, x=A + 2) == MISALIGNED
     assert ffn(L, nbytes=1024) == WORKSPACE

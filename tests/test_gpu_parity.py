@@ -15,8 +15,8 @@ import torch
 import oracle
 import sparse_moe_ffn_fp32_amd as moe
 from moe_inputs import LAYER_CONFIGS, make_config_inputs, make_layer_inputs
-from tests.gpu_util import (assert_out_close, check_routing, out_metrics, to_device,
-                            weights_args)
+from tests.gpu_util import (assert_out_close, check_routing, out_metrics, pack_reference,
+                            to_device, weights_args)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,11 +38,27 @@ def np_(t):
 
 # ---------------------------------------------------------------- library
 def test_native_library_is_loaded():
-    d = to_device(make_layer_inputs(4, 8, 2, seed=1, router_only=True))
+    d = to_device(make_layer_inputs(4, 8, 2, seed=1, router_only=True), pack=False)
     moe.route(d["x"], d["Wr"], d["br"], k=2)
     torch.cuda.synchronize()
     maps = open("/proc/self/maps").read()
     assert moe._native.LIB_PATH in maps
+
+
+# ---------------------------------------------------------------- packing
+@pytest.mark.parametrize("E,N", [(1, 64), (3, 192), (2, 2880), (1, 5760)])
+def test_pack_weights_layout(E, N):
+    rng = np.random.default_rng(E * 1000 + N)
+    codes = rng.integers(0, 256, size=(E, N, 1440), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(E, N, 90), dtype=np.uint8)
+    pc, ps = moe.pack_weights(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+    torch.cuda.synchronize()
+    want_c, want_s = pack_reference(codes, scales)
+    assert np.array_equal(np_(pc), want_c)
+    assert np.array_equal(np_(ps), want_s)
+    # a pure permutation: the byte histograms are unchanged
+    assert np.array_equal(np.bincount(np_(pc).ravel(), minlength=256),
+                          np.bincount(codes.ravel(), minlength=256))
 
 
 # ---------------------------------------------------------------- route
