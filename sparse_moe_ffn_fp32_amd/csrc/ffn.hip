@@ -243,11 +243,27 @@ static void launch_skinny(const FfnArgs& a, hipStream_t s) {
 // ------------------------------------------------------------------ wide
 constexpr int kWdBT = 128;     // tokens per tile (8 column tiles of 16)
 constexpr int kWdGroups = 4;   // 64-row groups per block, one per wave
-constexpr int kXsStride = 136; // bf16 per LDS activation row (128 K + 8 pad)
+constexpr int kXRow = 256;     // bytes per token row of an LDS activation stage (128 K)
+constexpr int kXStage = kWdBT * kXRow;   // 32 KiB
 
+// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Block = 4 waves = four 64-row groups x 128 tokens. Activations go straight
+// from global memory into a 2-stage LDS ring (global_load_lds, 16 bytes per
+// lane, no staging registers); within a 256-byte token row the 16-byte
+// pieces are XOR-swizzled by (token & 15), so the 16 token rows read by a
+// fragment load hit distinct banks. Weights stream to registers (2-step
+// ring) as in the skinny kernel. Per K step: wait for this step's loads,
+// barrier, issue the next activation stage, compute, refill the weights.
 template <int EPI, bool W_AS_B>
 __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kWdBT * kXsStride];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[2 * kXStage];
   __shared__ int slot_of[kWdBT];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -261,33 +277,30 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
     slot_of[tid] = p < re ? a.sorted_rows[p] : -1;
   }
 
-  // activation loader: chunk c = tid + 256q -> token (tid >> 4) + 16q, 16-byte
-  // piece tid & 15; padded tokens and the K tail are zero-filled
-  const int piece = tid & 15;
-  const uint16_t* gptr[8];
-  bool gok[8];
+  // Activation loads: wave w, instruction j fills LDS rows 4*(8w+j) .. +3
+  // (1 KiB); lane i takes token t = 4*(8w+j) + (i >> 4) and LDS piece
+  // q = i & 15, which holds K piece q ^ (t & 15). Padded tokens read the
+  // tile's first row (outputs dropped); the K tail re-reads the row's last
+  // piece (weights zero there), so all LDS values are finite.
+  const int q_lds = lane & 15;
+  const uint16_t* xsrc[8];
+  int xpiece[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int p = rb + (tid >> 4) + 16 * q;
-    gok[q] = p < re;
-    int row = 0;
-    if (gok[q]) row = a.gather ? a.sorted_rows[p] / a.k : p;
-    gptr[q] = a.act + (size_t)row * kH + piece * 8;
+  for (int j = 0; j < 8; ++j) {
+    const int t = 4 * (8 * wave + j) + (lane >> 4);
+    const int p = rb + t < re ? rb + t : rb;
+    const int row = a.gather ? a.sorted_rows[p] / a.k : p;
+    xsrc[j] = a.act + (size_t)row * kH;
+    xpiece[j] = q_lds ^ (t & 15);
   }
-  uint4 xr[8];
-  auto load_x = [&](int s) __attribute__((always_inline)) {
-    const bool kok = (s < kFullSteps) || piece < 8;
+  auto load_x = [&](int s, int stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      xr[q] = make_uint4(0, 0, 0, 0);
-      if (gok[q] && kok) xr[q] = *reinterpret_cast<const uint4*>(gptr[q] + s * 128);
-    }
-  };
-  auto store_x = [&](int stage) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int tt = (tid >> 4) + 16 * q;
-      *reinterpret_cast<uint4*>(&xs[stage][tt * kXsStride + piece * 8]) = xr[q];
+    for (int j = 0; j < 8; ++j) {
+      const int off = min(s * 128 + xpiece[j] * 8, kH - 8);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(xsrc[j] + off),
+          (__attribute__((address_space(3))) void*)(xs + stage * kXStage + (8 * wave + j) * 1024),
+          16, 0, 0);
     }
   };
 
@@ -305,7 +318,7 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int stage, int buf) __attribute__((always_inline)) {
-    const uint16_t* xsb = xs[stage];
+    const uint8_t* xsb = xs + stage * kXStage;
     float sf[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) sf[mt] = e8m0_to_f32((wsc[buf] >> (8 * mt)) & 0xFFu);
@@ -313,8 +326,10 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
     for (int i = 0; i < 4; ++i) {
       bf16x8 xf[8];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        xf[nt] = *reinterpret_cast<const bf16x8*>(&xsb[(16 * nt + r) * kXsStride + 32 * g + 8 * i]);
+      for (int nt = 0; nt < 8; ++nt) {
+        const int t = 16 * nt + r;
+        xf[nt] = *reinterpret_cast<const bf16x8*>(xsb + t * kXRow + (((4 * g + i) ^ r) * 16));
+      }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const bf16x8 wf = fp4x8_to_bf16x8(dword_of(wq[buf][mt], i), sf[mt]);
@@ -329,27 +344,28 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
     }
   };
 
-  load_x(0);
-  store_x(0);
-  load_x(1);
+  // Load issue order: W(0), W(1), X(0); then per step s: [X(s+1)] ... [W(s+2)].
+  // Before computing step s the loads still allowed in flight are those
+  // issued after X(s) and W(s): W(s+1) (5 loads per wave, or none when the
+  // wave holds no rows).
   if (w_ok) {
     wsrc.load(0, wq[0], wsc[0]);
     wsrc.load(1, wq[1], wsc[1]);
   }
-  __syncthreads();
-  // K loop, unrolled by two: LDS activation ring of 2, register weight ring of 2
+  load_x(0, 0);
   for (int s0 = 0; s0 < kSteps; s0 += 2) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int s = s0 + q;
       if (s < kSteps) {
-        if (s + 1 < kSteps) store_x(q ^ 1);
-        if (s + 2 < kSteps) load_x(s + 2);
+        if (s == 0 || !w_ok || s + 1 >= kSteps) wait_vmcnt<0>();
+        else wait_vmcnt<5>();
+        __builtin_amdgcn_s_barrier();
+        if (s + 1 < kSteps) load_x(s + 1, q ^ 1);
         if (w_ok) {
           compute(q, q);
           if (s + 2 < kSteps) wsrc.load(s + 2, wq[q], wsc[q]);
         }
-        __syncthreads();
       }
     }
   }
@@ -402,9 +418,13 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
 // ------------------------------------------------------------------ dispatch
 constexpr int kSkinnyMaxMeanRows = 24;
 
+bool ffn_uses_tiles(int n_rows, int E) {
+  return (long long)n_rows > (long long)kSkinnyMaxMeanRows * E;
+}
+
 hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s) {
   const int groups = a.N >> 6;
-  const bool skinny = (long long)n_rows <= (long long)kSkinnyMaxMeanRows * a.E;
+  const bool skinny = !ffn_uses_tiles(n_rows, a.E);
   if (skinny) {
     switch (epi) {
       case EPI_SWIGLU: launch_skinny<EPI_SWIGLU>(a, s); break;

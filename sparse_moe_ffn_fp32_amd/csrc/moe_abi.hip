@@ -21,7 +21,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t ids, w, counts, offsets, sorted, scratch, h, total;
+  size_t ids, w, counts, offsets, sorted, scratch, h, y, total;
 };
 
 bool sizes_ok(int T, int E, int k) {
@@ -40,6 +40,10 @@ WsLayout layout(int T, int E, int k) {
   l.sorted = off;   off = align_up(off + n * 4);
   l.scratch = off;  off = align_up(off + moe::route_scratch_bytes(T, E));
   l.h = off;        off = align_up(off + n * (size_t)moe::kI * 2);
+  // per-slot fp32 expert outputs: the many-rows schedule stores them and sums
+  // a token's k rows in a second pass instead of atomically adding into out
+  l.y = off;
+  if (n > 0 && moe::ffn_uses_tiles((int)n, E)) off = align_up(off + n * (size_t)moe::kH * 4);
   l.total = off;
   return l;
 }
@@ -279,17 +283,25 @@ moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
   float* scratch = reinterpret_cast<float*>(base + l.scratch);
   uint16_t* h = reinterpret_cast<uint16_t*>(base + l.h);
   const int n = T * k;
-  // router + top-k + softmax + expert permutation; also clears `out` for the
-  // accumulating down-projection epilogue
-  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, out, scratch, counts,
-                                         offsets, sorted, s), s));
+  // router + top-k + softmax + expert permutation
+  const bool tiles = moe::ffn_uses_tiles(n, E);
+  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, tiles ? nullptr : out,
+                                         scratch, counts, offsets, sorted, s), s));
   FfnArgs a13 = ffn_args(x, offsets, sorted, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
   a13.h_out = h;
   MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));
   FfnArgs a2 = ffn_args(h, offsets, sorted, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
-  a2.topk_w = w;
-  a2.out = out;
-  return after_launch(moe::launch_ffn(a2, moe::EPI_COMBINE, n, s), s);
+  if (!tiles) {
+    // few rows per expert: the down projection adds w * y into the cleared out
+    a2.topk_w = w;
+    a2.out = out;
+    return after_launch(moe::launch_ffn(a2, moe::EPI_COMBINE, n, s), s);
+  }
+  // many rows: store y per slot, then out[t] = sum_j w[t, j] y[t*k + j]
+  float* y = reinterpret_cast<float*>(base + l.y);
+  a2.y_out = y;
+  MOE_TRY(after_launch(moe::launch_ffn(a2, moe::EPI_STORE_Y, n, s), s));
+  return after_launch(moe::launch_combine(y, w, T, k, out, s), s);
 }
 
 }  // extern "C"

@@ -47,6 +47,7 @@ hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* counts, int
 // Picks the weight-streaming (few rows per expert) or the tiled (many rows)
 // grouped GEMM from the mean rows per expert, n_rows / E.
 hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s);
+bool ffn_uses_tiles(int n_rows, int E);
 
 hipError_t launch_combine(const float* y, const float* w, int T, int k, float* out, hipStream_t s);
 

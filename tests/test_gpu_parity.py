@@ -280,3 +280,20 @@ def test_forward_config_sampled(idx):
     ref = oracle.forward(inp, c.k, tokens=sample, ids_override=ids_h)
     m = assert_out_close(np_(out)[sample], ref["out"], c.name)
     say(f"  sampled metrics {m}; fused vs unfused {m_all}; near-tie tokens with another set: {n_tie}")
+
+
+@pytest.mark.parametrize("T,E,k", [(16, 32, 4), (256, 8, 4)])
+def test_gate_up_and_down_accumulate_onto_residual(T, E, k):
+    """The two halves as separate calls; the down half adds into a residual."""
+    say(f"gate_up + down_accumulate T={T} E={E} k={k}")
+    inp = make_layer_inputs(T, E, k, seed=3000 + T + E)
+    d = to_device(inp)
+    ids, w, counts, offsets, rows = _gpu_route_and_permute(d, E, k)
+    p13c, p13s, b13, p2c, p2s, b2 = weights_args(d)
+    h = moe.gate_up(d["x"], offsets, rows, p13c, p13s, b13, k=k)
+    resid = torch.randn((T, 2880), dtype=torch.float32, device="cuda")
+    out = resid.clone()
+    moe.down_accumulate(h, offsets, rows, w, p2c, p2s, b2, out=out, k=k)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp, k, ids_override=np_(ids))
+    assert_out_close(np_(out) - np_(resid).astype(np.float64), ref["out"], "down_accumulate")
