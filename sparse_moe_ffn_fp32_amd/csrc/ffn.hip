@@ -241,10 +241,33 @@ static void launch_skinny(const FfnArgs& a, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ wide
-constexpr int kWdBT = 128;     // tokens per tile (8 column tiles of 16)
+
+constexpr int kTileChunk = 8;   // token tiles that share a pass over the weight columns
+constexpr int kXcds = 8;
+
+// Work order of the tiled kernel. Workgroups are dealt to the 8 XCDs
+// round-robin in launch order, and each XCD has its own L2, so the linear
+// block id is first turned into an order in which every XCD runs one
+// contiguous range of the work. Within that order, kTileChunk consecutive
+// token tiles go with each weight column block in turn (tiles fastest): the
+// tiles of a chunk read the same weights close together in time on one L2.
+__device__ __forceinline__ void wide_work_item(int gx, int gy, int& wx, int& ty) {
+  const int nb = gx * gy;
+  const int b = blockIdx.x;
+  const int q = nb / kXcds, r = nb % kXcds, xcd = b % kXcds, idx = b / kXcds;
+  const int L = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+  const int per = gx * kTileChunk;
+  const int chunk = L / per, rem = L - chunk * per;
+  const int cy = min(kTileChunk, gy - chunk * kTileChunk);
+  wx = rem / cy;
+  ty = chunk * kTileChunk + (rem - wx * cy);
+}
+constexpr int kWdNT = 4;           // 16-token column tiles per wave
+constexpr int kWdBT = 16 * kWdNT;   // tokens per tile
 constexpr int kWdGroups = 4;   // 64-row groups per block, one per wave
 constexpr int kXRow = 256;     // bytes per token row of an LDS activation stage (128 K)
-constexpr int kXStage = kWdBT * kXRow;   // 32 KiB
+constexpr int kXStage = kWdBT * kXRow;   // 16 KiB
+constexpr int kXLoads = kWdBT / 16;   // 1 KiB LDS DMA instructions per wave per stage
 
 // s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maxima).
@@ -254,7 +277,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Block = 4 waves = four 64-row groups x 128 tokens. Activations go straight
+// Block = 4 waves = four 64-row groups x 64 tokens. Activations go straight
 // from global memory into a 2-stage LDS ring (global_load_lds, 16 bytes per
 // lane, no staging registers); within a 256-byte token row the 16-byte
 // pieces are XOR-swizzled by (token & 15), so the 16 token rows read by a
@@ -269,25 +292,28 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   int e, rb, re;
-  if (!find_tile(a.offsets, a.E, kWdBT, blockIdx.y, e, rb, re)) return;
-  const int G = blockIdx.x * kWdGroups + wave;
+  int wx, ty;
+  const int gx = ((a.N >> 6) + kWdGroups - 1) / kWdGroups;
+  wide_work_item(gx, gridDim.x / gx, wx, ty);
+  if (!find_tile(a.offsets, a.E, kWdBT, ty, e, rb, re)) return;
+  const int G = wx * kWdGroups + wave;
   const bool w_ok = G < (a.N >> 6);
   if (tid < kWdBT) {
     const int p = rb + tid;
     slot_of[tid] = p < re ? a.sorted_rows[p] : -1;
   }
 
-  // Activation loads: wave w, instruction j fills LDS rows 4*(8w+j) .. +3
-  // (1 KiB); lane i takes token t = 4*(8w+j) + (i >> 4) and LDS piece
+  // Activation loads: wave w, instruction j fills LDS rows 4*(4w+j) .. +3
+  // (1 KiB); lane i takes token t = 4*(4w+j) + (i >> 4) and LDS piece
   // q = i & 15, which holds K piece q ^ (t & 15). Padded tokens read the
   // tile's first row (outputs dropped); the K tail re-reads the row's last
   // piece (weights zero there), so all LDS values are finite.
   const int q_lds = lane & 15;
-  const uint16_t* xsrc[8];
-  int xpiece[8];
+  const uint16_t* xsrc[kXLoads];
+  int xpiece[kXLoads];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int t = 4 * (8 * wave + j) + (lane >> 4);
+  for (int j = 0; j < kXLoads; ++j) {
+    const int t = 4 * (kXLoads * wave + j) + (lane >> 4);
     const int p = rb + t < re ? rb + t : rb;
     const int row = a.gather ? a.sorted_rows[p] / a.k : p;
     xsrc[j] = a.act + (size_t)row * kH;
@@ -295,11 +321,11 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
   }
   auto load_x = [&](int s, int stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kXLoads; ++j) {
       const int off = min(s * 128 + xpiece[j] * 8, kH - 8);
       __builtin_amdgcn_global_load_lds(
           (const void*)(xsrc[j] + off),
-          (__attribute__((address_space(3))) void*)(xs + stage * kXStage + (8 * wave + j) * 1024),
+          (__attribute__((address_space(3))) void*)(xs + stage * kXStage + (kXLoads * wave + j) * 1024),
           16, 0, 0);
     }
   };
@@ -311,11 +337,11 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
   const int r = lane & 15;
   const int g = lane >> 4;
 
-  f32x4 acc[4][8];
+  f32x4 acc[4][kWdNT];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < kWdNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int stage, int buf) __attribute__((always_inline)) {
     const uint8_t* xsb = xs + stage * kXStage;
@@ -324,9 +350,9 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
     for (int mt = 0; mt < 4; ++mt) sf[mt] = e8m0_to_f32((wsc[buf] >> (8 * mt)) & 0xFFu);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      bf16x8 xf[8];
+      bf16x8 xf[kWdNT];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
+      for (int nt = 0; nt < kWdNT; ++nt) {
         const int t = 16 * nt + r;
         xf[nt] = *reinterpret_cast<const bf16x8*>(xsb + t * kXRow + (((4 * g + i) ^ r) * 16));
       }
@@ -334,7 +360,7 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
       for (int mt = 0; mt < 4; ++mt) {
         const bf16x8 wf = fp4x8_to_bf16x8(dword_of(wq[buf][mt], i), sf[mt]);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
+        for (int nt = 0; nt < kWdNT; ++nt) {
           if constexpr (W_AS_B)
             acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[nt], wf, acc[mt][nt], 0, 0, 0);
           else
@@ -381,7 +407,7 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = bf16_bits_to_f32(bias[R0 + j]);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
+      for (int nt = 0; nt < kWdNT; ++nt) {
         const int p = rb + 16 * nt + r;
         if (p >= re) continue;
         const f32x4& c = acc[mt][nt];
@@ -398,7 +424,7 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
       const int f = G * 64 + 16 * mt + r;
       const float bf = bf16_bits_to_f32(bias[f]);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
+      for (int nt = 0; nt < kWdNT; ++nt) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int slot = slot_of[16 * nt + 4 * g + j];
@@ -433,7 +459,7 @@ hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s)
     }
   } else {
     const int tiles = (n_rows + kWdBT - 1) / kWdBT + min(a.E, n_rows);
-    const dim3 grid((groups + kWdGroups - 1) / kWdGroups, tiles);
+    const dim3 grid(((groups + kWdGroups - 1) / kWdGroups) * tiles);
     switch (epi) {
       case EPI_SWIGLU: hipLaunchKernelGGL((ffn_wide_kernel<EPI_SWIGLU, false>), grid, dim3(256), 0, s, a); break;
       case EPI_COMBINE: hipLaunchKernelGGL((ffn_wide_kernel<EPI_COMBINE, true>), grid, dim3(256), 0, s, a); break;
