@@ -118,19 +118,17 @@ struct SkStage {
   uint4 xv[4];
 };
 
-// Grid (RG consecutive 64-row groups, expert e). One wave streams RG groups
+// One work item: RG consecutive 64-row groups G0.. of expert e. One wave streams RG groups
 // (64*RG rows: the activations it reads are shared by all of them). The
 // weight stream needs no routing data, so the wave only waits for the
 // expert's row range and its first row lookups before the stream starts; a
 // dependent load issued behind the chip-wide weight traffic would wait for
 // the whole in-flight volume. An expert with more than 16 rows is handled 16
 // at a time.
-template <int EPI, int RG>
-__global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
+template <int EPI, int RG, class WaitAct>
+__device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, const WaitAct& wait_act) {
   constexpr int MT = 4 * RG;
   const int lane = threadIdx.x;
-  const int G0 = blockIdx.x * RG;
-  const int e = blockIdx.y;
   const int r = lane & 15;   // weight row in a 16-row tile / token column
   const int g = lane >> 4;   // lane group: MX block 4s + g of step s
   const int e_begin = a.offsets[e];
@@ -148,6 +146,9 @@ __global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
     const bool tok_ok = p < re;
     // padded token columns read the tile's first row: their outputs are dropped
     const int slot = a.sorted_rows[tok_ok ? p : rb];
+    // the routing weight is fetched with the row lookups, not behind the stream
+    float wt = 0.f;
+    if constexpr (EPI == EPI_COMBINE) wt = a.topk_w[slot];
     const int arow = a.gather ? slot / a.k : (tok_ok ? p : rb);
     const uint16_t* xp = a.act + (size_t)arow * kH;
     // slot >= 0 always; the compiler cannot know it, so the weight addresses
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
 
     // s is a compile-time constant after unrolling; the K tail (blocks >= 90)
     // re-reads block 89, whose weights are zero there
-    auto issue = [&](SkStage<RG>& st, int s) __attribute__((always_inline)) {
+    auto issue_w = [&](SkStage<RG>& st, int s) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         uint4 w4[4];
@@ -166,6 +167,8 @@ __global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) st.w[4 * q + mt] = w4[mt];
       }
+    };
+    auto issue_x = [&](SkStage<RG>& st, int s) __attribute__((always_inline)) {
       const int kb = min(4 * s + g, kKB - 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.xv[i] = *reinterpret_cast<const uint4*>(xp + kb * 32 + 8 * i);
@@ -191,13 +194,20 @@ __global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
     };
 
     // fully unrolled K loop with a kSkDepth-step register prefetch ring
+    // (the first weight stages go out before the activations may be read)
     SkStage<RG> st[kSkDepth];
 #pragma unroll
-    for (int q = 0; q < kSkDepth; ++q) issue(st[q], q);
+    for (int q = 0; q < kSkDepth; ++q) issue_w(st[q], q);
+    if (rb == e_begin) wait_act();
+#pragma unroll
+    for (int q = 0; q < kSkDepth; ++q) issue_x(st[q], q);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       compute(st[s % kSkDepth]);
-      if (s + kSkDepth < kSteps) issue(st[s % kSkDepth], s + kSkDepth);
+      if (s + kSkDepth < kSteps) {
+        issue_w(st[s % kSkDepth], s + kSkDepth);
+        issue_x(st[s % kSkDepth], s + kSkDepth);
+      }
     }
 
     // 16x16 result: lane holds token column r and weight rows 4g + j of each tile.
@@ -214,7 +224,6 @@ __global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
           const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(v2, v3));
           *reinterpret_cast<uint32_t*>(a.h_out + (size_t)p * kI + R0 / 2) = h0 | (h1 << 16);
         } else if constexpr (EPI == EPI_COMBINE) {
-          const float wt = a.topk_w[slot];
           float* o = a.out + (size_t)(slot / a.k) * kH + R0;
           unsafeAtomicAdd(o + 0, wt * v0);
           unsafeAtomicAdd(o + 1, wt * v1);
@@ -226,6 +235,16 @@ __global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
       }
     }
   }
+}
+
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
+// Grid (RG-group items, expert e).
+template <int EPI, int RG>
+__global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
+  skinny_item<EPI, RG>(a, blockIdx.x * RG, blockIdx.y, NoWait{});
 }
 
 // Two groups per wave halve the activation reads per weight byte, but only
