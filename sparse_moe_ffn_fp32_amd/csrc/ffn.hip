@@ -307,6 +307,8 @@ template <int EPI, bool W_AS_B>
 __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t xs[2 * kXStage];
   __shared__ int slot_of[kWdBT];
+  __shared__ uint16_t bias_s[kWdGroups * 64];
+  static_assert(kWdGroups * 64 == 256, "one bias per thread");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -320,6 +322,12 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
   if (tid < kWdBT) {
     const int p = rb + tid;
     slot_of[tid] = p < re ? a.sorted_rows[p] : -1;
+  }
+  // the block's 256 output-row biases go to LDS now; loaded in the epilogue
+  // they would wait behind the tail of the weight stream
+  {
+    const int row = wx * kWdGroups * 64 + tid;
+    bias_s[tid] = row < a.N ? a.bias[(size_t)e * a.N + row] : 0;
   }
 
   // Activation loads: wave w, instruction j fills LDS rows 4*(4w+j) .. +3
@@ -416,7 +424,6 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
   }
   if (!w_ok) return;
 
-  const uint16_t* bias = a.bias + (size_t)e * a.N;
   if constexpr (!W_AS_B) {
     // D[weight row][token]: lane holds token column r, rows 4g + j of tile mt
 #pragma unroll
@@ -424,7 +431,7 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
       const int R0 = G * 64 + 16 * mt + 4 * g;
       float b[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = bf16_bits_to_f32(bias[R0 + j]);
+      for (int j = 0; j < 4; ++j) b[j] = bf16_bits_to_f32(bias_s[wave * 64 + 16 * mt + 4 * g + j]);
 #pragma unroll
       for (int nt = 0; nt < kWdNT; ++nt) {
         const int p = rb + 16 * nt + r;
@@ -441,7 +448,7 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int f = G * 64 + 16 * mt + r;
-      const float bf = bf16_bits_to_f32(bias[f]);
+      const float bf = bf16_bits_to_f32(bias_s[wave * 64 + 16 * mt + r]);
 #pragma unroll
       for (int nt = 0; nt < kWdNT; ++nt) {
 #pragma unroll

@@ -132,11 +132,16 @@ __device__ __forceinline__ void route_kloop(const RouteLoader<MT>& L, f32x16 (&a
   RStage<MT> st[D];
 #pragma unroll
   for (int q = 0; q < D; ++q) L.load(st[q], q);
+  // scheduling barriers keep the ring's loads where they are written: left
+  // free, the scheduler sinks them next to their use and only about one
+  // step stays in flight
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (NSTEPS <= 16) {
 #pragma unroll
     for (int s = 0; s < NSTEPS; ++s) {
       route_mma<MT>(st[s % D], acc);
       if (s + D < NSTEPS) L.load(st[s % D], s + D);
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     for (int s0 = 0; s0 < NSTEPS; s0 += D) {
@@ -147,6 +152,7 @@ __device__ __forceinline__ void route_kloop(const RouteLoader<MT>& L, f32x16 (&a
           route_mma<MT>(st[q], acc);
           if (s + D < NSTEPS) L.load(st[q], s + D);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
