@@ -43,6 +43,12 @@ hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, int E, int N
 
 hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_rows, hipStream_t s);
+// Same permutation from per-block expert histograms hist[nb][E] of
+// consecutive slot ranges of spb slots each (spb <= 256); hist is
+// overwritten (it becomes the blocks' base positions).
+hipError_t launch_permute_blocks(const int32_t* ids, int n, int E, int32_t* hist, int nb, int spb,
+                                 int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
+                                 hipStream_t s);
 
 // Picks the weight-streaming (few rows per expert) or the tiled (many rows)
 // grouped GEMM from the mean rows per expert, n_rows / E.

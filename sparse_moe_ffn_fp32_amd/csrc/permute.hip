@@ -22,6 +22,123 @@ hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* counts, int
   return hipGetLastError();
 }
 
+// Parallel form of the same stable permutation when the router already
+// counted its routed slots per block: route block b owns slots
+// [b*spb, (b+1)*spb) (spb <= 256) and hist[b][e] counts them by expert.
+// permute_scan_kernel (one workgroup) turns the histograms into counts,
+// offsets and base[b][e] = offsets[e] + (slots of e in blocks before b), in
+// place; permute_scatter_kernel (one workgroup per route block) ranks its
+// slots within each expert and writes them. Slots go in ascending order
+// within an expert, as in the single-workgroup version.
+constexpr int kScanThreads = 1024;
+constexpr int kScatterThreads = 256;
+
+__global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int E, int32_t* __restrict__ hist,
+                                                                    int nb,
+                                                                    int32_t* __restrict__ counts,
+                                                                    int32_t* __restrict__ offsets) {
+  // thread (segment s, expert e): blocks [s*per, (s+1)*per) of expert e
+  __shared__ int seg_sum[kScanThreads];
+  __shared__ int excl_e[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  const int nseg = kScanThreads / E;   // E <= 256, so at least 4 segments
+  const int e = tid % E, sgm = tid / E;
+  const bool act = sgm < nseg;
+  const int per = (nb + nseg - 1) / nseg;
+  const int b0 = min(nb, sgm * per), b1 = min(nb, b0 + per);
+  int sum = 0;
+  if (act) {
+#pragma unroll 16
+    for (int b = b0; b < b1; ++b) sum += hist[(size_t)b * E + e];
+  }
+  seg_sum[tid] = act ? sum : 0;
+  __syncthreads();
+  if (tid < E) {
+    int tot = 0;
+    for (int q = 0; q < nseg; ++q) tot += seg_sum[q * E + tid];
+    excl_e[tid] = tot;   // totals; scanned below
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // exclusive scan over experts: 4 per lane, then across the wave
+    int c[4], local = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ee = tid * 4 + q;
+      c[q] = ee < E ? excl_e[ee] : 0;
+      local += c[q];
+    }
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (tid >= d) incl += v;
+    }
+    int run = incl - local;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ee = tid * 4 + q;
+      if (ee < E) {
+        counts[ee] = c[q];
+        offsets[ee] = run;
+        excl_e[ee] = run;
+      }
+      run += c[q];
+    }
+    if (tid == 63) offsets[E] = incl;
+  }
+  __syncthreads();
+  if (act) {
+    int run = excl_e[e];
+    for (int q = 0; q < sgm; ++q) run += seg_sum[q * E + e];
+    for (int b = b0; b < b1; ++b) {
+      const int h = hist[(size_t)b * E + e];
+      hist[(size_t)b * E + e] = run;
+      run += h;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, int n, int E, const int32_t* __restrict__ base, int spb,
+    int32_t* __restrict__ sorted_rows) {
+  __shared__ int wcnt[kScatterThreads / 64][kMaxExperts];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int e = lane; e < kMaxExperts; e += 64) wcnt[wave][e] = 0;
+  const int i = blockIdx.x * spb + tid;
+  int e = -1;
+  if (tid < spb && i < n) e = ids[i];
+  const bool valid = e >= 0 && e < E;
+  unsigned long long peers = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const bool on = valid && ((e >> bit) & 1);
+    const unsigned long long bal = __ballot(on);
+    peers &= on ? bal : ~bal;
+  }
+  const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+  if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);
+  __syncthreads();
+  if (valid) {
+    int p = base[(size_t)blockIdx.x * E + e] + rank;
+    for (int w = 0; w < wave; ++w) p += wcnt[w][e];
+    sorted_rows[p] = i;
+  }
+}
+
+hipError_t launch_permute_blocks(const int32_t* ids, int n, int E, int32_t* hist, int nb, int spb,
+                                 int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
+                                 hipStream_t s) {
+  if (spb > kScatterThreads || E > kMaxExperts) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, E, hist, nb, counts,
+                     offsets);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kScatterThreads), 0, s, ids, n, E, hist,
+                     spb, sorted_rows);
+  return hipGetLastError();
+}
+
 // out[t, :] = sum_j w[t*k + j] * y[t*k + j, :]  (weighted sum of the selected
 // experts' outputs; one thread per 4 output elements).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,

@@ -35,7 +35,9 @@ static_assert(kRouteChunkSteps * 16 * kRouteChunks == kH, "chunks must tile K");
 static bool few_tokens(int T, int E) { return T <= kRouteSmallT && T * E <= kRouteMaxPairs; }
 
 size_t route_scratch_bytes(int T, int E) {
-  return few_tokens(T, E) ? (size_t)kRouteChunks * T * E * sizeof(float) : 0;
+  // few tokens: K-chunk partial logits; many: per-32-token-block expert histograms
+  return few_tokens(T, E) ? (size_t)kRouteChunks * T * E * sizeof(float)
+                          : (size_t)((T + 31) / 32) * E * sizeof(int32_t);
 }
 
 __device__ __forceinline__ void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
@@ -260,7 +262,8 @@ __global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restri
                                                         int k, int32_t* __restrict__ ids,
                                                         float* __restrict__ wts,
                                                         float* __restrict__ logits,
-                                                        float* __restrict__ zero_out) {
+                                                        float* __restrict__ zero_out,
+                                                        int32_t* __restrict__ block_hist) {
   constexpr int KW = kH / WK;      // K range of one wave
   constexpr int KSTEPS = KW / 16;  // MFMA steps of one wave
   constexpr int LDR = 33;          // padded row of the reduction buffer
@@ -313,6 +316,17 @@ __global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restri
                            nullptr);
   }
   if (zero_out) zero_rows_slice(zero_out, T, blockIdx.x, gridDim.x, threadIdx.x, WK * 64);
+  if (block_hist) {
+    // expert histogram of this block's routed slots, for the parallel permutation
+    int* hist = reinterpret_cast<int*>(red);   // the logits tile is no longer needed
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += WK * 64) hist[e] = 0;
+    __syncthreads();
+    const int nslots = (min(T, tok0 + 32) - tok0) * k;
+    for (int i = threadIdx.x; i < nslots; i += WK * 64) atomicAdd(&hist[ids[(size_t)tok0 * k + i]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += WK * 64) block_hist[(size_t)blockIdx.x * E + e] = hist[e];
+  }
 }
 
 // ---------------------------------------------------------------- few tokens
@@ -454,23 +468,25 @@ static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const floa
   }
   const int blocks = (T + 31) / 32;
   const size_t lds = (size_t)MT * 32 * 33 * sizeof(float);
+  static_assert(32 * 33 >= kMaxExperts, "the reduction tile doubles as the histogram");
+  int32_t* hist = reinterpret_cast<int32_t*>(scratch);   // [blocks][E] routed-slot histograms
   // 12 waves split K when few blocks would run; only for one expert tile,
   // where the 768-thread register budget holds the prefetch ring.
   if constexpr (MT == 1) {
     if (blocks < 256) {
       hipLaunchKernelGGL((route_kernel<1, 12>), dim3(blocks), dim3(12 * 64), lds, s, x, Wr, br, T, E,
-                         k, ids, w, logits, zero_out);
+                         k, ids, w, logits, zero_out, counts ? hist : nullptr);
     } else {
       hipLaunchKernelGGL((route_kernel<1, 4>), dim3(blocks), dim3(4 * 64), lds, s, x, Wr, br, T, E,
-                         k, ids, w, logits, zero_out);
+                         k, ids, w, logits, zero_out, counts ? hist : nullptr);
     }
   } else {
     hipLaunchKernelGGL((route_kernel<MT, 4>), dim3(blocks), dim3(4 * 64), lds, s, x, Wr, br, T, E, k,
-                       ids, w, logits, zero_out);
+                       ids, w, logits, zero_out, counts ? hist : nullptr);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !counts) return err;
-  return launch_permute(ids, T * k, E, counts, offsets, sorted_rows, s);
+  return launch_permute_blocks(ids, T * k, E, hist, blocks, 32 * k, counts, offsets, sorted_rows, s);
 }
 
 hipError_t launch_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
