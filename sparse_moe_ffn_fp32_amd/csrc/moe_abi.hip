@@ -184,7 +184,9 @@ moe_status_t moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* 
   MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(moe::launch_permute(topk_ids, T * k, E, counts, offsets, sorted_rows, s), s);
+  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + layout(T, E, k).scratch);
+  return after_launch(moe::launch_permute(topk_ids, T * k, E, k, counts, offsets, sorted_rows, hist, s),
+                      s);
 }
 
 moe_status_t moe_expert_ffn(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_rows,

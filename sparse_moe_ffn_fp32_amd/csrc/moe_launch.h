@@ -41,8 +41,11 @@ size_t route_scratch_bytes(int T, int E);
 hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, int E, int N, uint8_t* pcodes,
                        uint8_t* pscales, hipStream_t s);
 
-hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* sorted_rows, hipStream_t s);
+// Stable permutation of n = T*k slots. Up to 1024 slots (or without hist):
+// one workgroup; above: a histogram pass into hist (ceil(T/32)*E ints), a
+// scan and a parallel scatter.
+hipError_t launch_permute(const int32_t* ids, int n, int E, int k, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_rows, int32_t* hist, hipStream_t s);
 // Same permutation from per-block expert histograms hist[nb][E] of
 // consecutive slot ranges of spb slots each (spb <= 256); hist is
 // overwritten (it becomes the blocks' base positions).

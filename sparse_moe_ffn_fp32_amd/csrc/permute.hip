@@ -15,12 +15,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
   block_permute(ids, n, E, counts, offsets, sorted_rows, sm);
 }
 
-hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* sorted_rows, hipStream_t s) {
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, n, E, counts, offsets,
-                     sorted_rows);
-  return hipGetLastError();
-}
+
 
 // Parallel form of the same stable permutation when the router already
 // counted its routed slots per block: route block b owns slots
@@ -128,6 +123,24 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
   }
 }
 
+// Expert histogram of each block's spb consecutive slots (the standalone
+// permutation's first pass; the router writes the same table as it goes).
+__global__ __launch_bounds__(kScatterThreads) void permute_hist_kernel(const int32_t* __restrict__ ids,
+                                                                       int n, int E, int spb,
+                                                                       int32_t* __restrict__ hist) {
+  __shared__ int h[kMaxExperts];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kMaxExperts; e += kScatterThreads) h[e] = 0;
+  __syncthreads();
+  const int i = blockIdx.x * spb + tid;
+  if (tid < spb && i < n) {
+    const int e = ids[i];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kScatterThreads) hist[(size_t)blockIdx.x * E + e] = h[e];
+}
+
 hipError_t launch_permute_blocks(const int32_t* ids, int n, int E, int32_t* hist, int nb, int spb,
                                  int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
                                  hipStream_t s) {
@@ -137,6 +150,20 @@ hipError_t launch_permute_blocks(const int32_t* ids, int n, int E, int32_t* hist
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kScatterThreads), 0, s, ids, n, E, hist,
                      spb, sorted_rows);
   return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t* ids, int n, int E, int k, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_rows, int32_t* hist, hipStream_t s) {
+  if (n <= kPermThreads || !hist) {
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, n, E, counts, offsets,
+                       sorted_rows);
+    return hipGetLastError();
+  }
+  // slots in blocks of 32 tokens, as the router's histograms
+  const int spb = 32 * k;
+  const int nb = (n + spb - 1) / spb;
+  hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(kScatterThreads), 0, s, ids, n, E, spb, hist);
+  return launch_permute_blocks(ids, n, E, hist, nb, spb, counts, offsets, sorted_rows, s);
 }
 
 // out[t, :] = sum_j w[t*k + j] * y[t*k + j, :]  (weighted sum of the selected
