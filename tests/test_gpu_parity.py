@@ -139,6 +139,8 @@ SMALL_CASES = [
     (130, 4, 4),    # tiled: 128-row tile + ragged tail
     (300, 4, 1),    # tiled, k = 1
     (256, 8, 4),
+    (192, 32, 4),   # weight-streaming kernels behind the many-token router (T > 128)
+    (300, 64, 4),   # the same with two expert tiles in the router
 ]
 
 
