@@ -17,6 +17,10 @@ bytes (decode) or FLOPs (prefill) divided by that time give `achieved`.
 
 cpu_baseline: the fp64 oracle on a bounded sample of the same workload, on
 the host cores (not a tuned CPU implementation).
+
+Also reported: p10/p50/p90 of single steps (a second pass with one event
+pair per step) and, for the weight-bound shapes, the step time without
+rotating weight copies.
 """
 from __future__ import annotations
 
@@ -167,6 +171,28 @@ def main() -> int:
     log(f"bench: {ms_per_step * 1e3:.1f} us per step")
     assert torch.isfinite(out).all().item(), "non-finite layer output"
 
+    # Distribution of single steps (a second pass, one event pair per step),
+    # and for the weight-bound shapes the same layer without rotating the
+    # weight copies (one copy, partly served from the Infinity Cache).
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    p10, p50, p90 = (float(v) for v in np.percentile(per_step, [10, 50, 90]))
+    nonrot_ms = None
+    if copies > 1:
+        n0 = torch.cuda.Event(enable_timing=True)
+        n1 = torch.cuda.Event(enable_timing=True)
+        n0.record(stream)
+        for i in range(args.steps):
+            step(0)
+        n1.record(stream)
+        torch.cuda.synchronize()
+        nonrot_ms = n0.elapsed_time(n1) / args.steps
+
     # Dominant kernel: the gate/up GEMM, timed by HIP events on its stream
     # around K back-to-back launches (the routing is computed once; each
     # launch streams the next weight copy).
@@ -235,6 +261,8 @@ def main() -> int:
         "roofline": roof,
         "layer_roofline_frac": round(layer_frac, 4),
         "experts_touched": touched,
+        "step_ms_p10_p50_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
+        "ms_per_step_one_weight_copy": None if nonrot_ms is None else round(nonrot_ms, 5),
     }
     if not args.no_cpu_baseline:
         n = args.cpu_tokens or (cfg.T if cfg.T <= 64 else (32 if E <= 32 else 16))
