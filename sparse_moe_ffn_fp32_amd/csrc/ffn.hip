@@ -125,14 +125,61 @@ struct SkStage {
 // dependent load issued behind the chip-wide weight traffic would wait for
 // the whole in-flight volume. An expert with more than 16 rows is handled 16
 // at a time.
+// Position of the n-th set bit (n < popcount) of a 64-bit mask.
+__device__ __forceinline__ int nth_set_bit(unsigned long long m, int n) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) {
+    const int c = __popcll(m & ((1ull << w) - 1ull));
+    if (n >= c) {
+      n -= c;
+      m >>= w;
+      pos += w;
+    }
+  }
+  return pos;
+}
+
+// Expert e's slots straight from the routing ids: `below` = slots of lower
+// experts (e's first position in the stable expert order), `count` = e's
+// slots, and for lane r the slot of rank rank0 + (r & 15) among e's slots in
+// slot order (-1 past the end). One pass of coalesced loads, no dependent
+// lookups; every lane of the wave must call it.
+__device__ __forceinline__ void scan_expert_slots(const int32_t* ids, int n, int e, int rank0,
+                                                  int& below, int& count, int& slot_r) {
+  const int lane = threadIdx.x & 63;
+  const int tr = rank0 + (lane & 15);
+  below = 0;
+  count = 0;
+  slot_r = -1;
+#pragma unroll 4
+  for (int c = 0; c < n; c += 64) {
+    const int i = c + lane;
+    const int id = i < n ? ids[i] : 0x7FFFFFFF;
+    const unsigned long long eq = __ballot(id == e);
+    below += __popcll(__ballot(id < e));
+    const int in = __popcll(eq);
+    if (tr >= count && tr < count + in) slot_r = c + nth_set_bit(eq, tr - count);
+    count += in;
+  }
+}
+
 template <int EPI, int RG, class WaitAct>
 __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, const WaitAct& wait_act) {
   constexpr int MT = 4 * RG;
   const int lane = threadIdx.x;
   const int r = lane & 15;   // weight row in a 16-row tile / token column
   const int g = lane >> 4;   // lane group: MX block 4s + g of step s
-  const int e_begin = a.offsets[e];
-  const int e_end = a.offsets[e + 1];
+  int e_begin, e_end, slot_first = -1;
+  if (a.ids) {
+    int below, count;
+    scan_expert_slots(a.ids, a.n_slots, e, 0, below, count, slot_first);
+    e_begin = below;
+    e_end = below + count;
+  } else {
+    e_begin = a.offsets[e];
+    e_end = a.offsets[e + 1];
+  }
   if (e_end <= e_begin) return;
   // biases of this lane's output rows (consumed by the epilogue)
   const uint16_t* bias = a.bias + (size_t)e * a.N + G0 * 64 + 4 * g;
@@ -145,7 +192,18 @@ __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, con
     const int p = rb + r;
     const bool tok_ok = p < re;
     // padded token columns read the tile's first row: their outputs are dropped
-    const int slot = a.sorted_rows[tok_ok ? p : rb];
+    int slot;
+    if (a.ids) {
+      int sr = slot_first;
+      if (rb != e_begin) {
+        int b2, c2;
+        scan_expert_slots(a.ids, a.n_slots, e, rb - e_begin, b2, c2, sr);
+      }
+      const int tile_first = __shfl(sr, 0, 64);
+      slot = tok_ok ? sr : tile_first;
+    } else {
+      slot = a.sorted_rows[tok_ok ? p : rb];
+    }
     // the routing weight is fetched with the row lookups, not behind the stream
     float wt = 0.f;
     if constexpr (EPI == EPI_COMBINE) wt = a.topk_w[slot];

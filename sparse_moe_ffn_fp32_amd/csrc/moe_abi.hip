@@ -287,14 +287,22 @@ moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
   const int n = T * k;
   // router + top-k + softmax + expert permutation
   const bool tiles = moe::ffn_uses_tiles(n, E);
+  // The weight-streaming schedule needs no permutation arrays: its waves
+  // find their slots in the routing ids.
   MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, tiles ? nullptr : out,
-                                         scratch, counts, offsets, sorted, s), s));
+                                         scratch, tiles ? counts : nullptr, offsets, sorted, s), s));
   FfnArgs a13 = ffn_args(x, offsets, sorted, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
   a13.h_out = h;
+  if (!tiles) {
+    a13.ids = ids;
+    a13.n_slots = n;
+  }
   MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));
   FfnArgs a2 = ffn_args(h, offsets, sorted, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
   if (!tiles) {
     // few rows per expert: the down projection adds w * y into the cleared out
+    a2.ids = ids;
+    a2.n_slots = n;
     a2.topk_w = w;
     a2.out = out;
     return after_launch(moe::launch_ffn(a2, moe::EPI_COMBINE, n, s), s);

@@ -27,6 +27,11 @@ struct FfnArgs {
   int E;
   int k;
   int gather;                   // 1: activation row = sorted_rows[p] / k, 0: row p
+  // Weight-streaming kernels only: when not null, each wave finds its
+  // expert's slots in the routing ids [n_slots] itself (same stable order and
+  // positions as the permutation) and offsets / sorted_rows are not read.
+  const int32_t* ids;
+  int n_slots;
 };
 
 // Router + top-k + softmax. `zero_out` (optional) is cleared for the
