@@ -24,10 +24,13 @@
 //    one or two 64-row groups of one expert and its tokens, 16 at a time;
 //    it streams the groups' code bytes front to back with a 3-step register
 //    prefetch and reads its activations directly (L2-resident).
+//    In the layer's own schedule the wave finds its expert's slots in the
+//    routing ids; through the standalone entry points it reads offsets /
+//    sorted_rows.
 //  * tiled ("wide", many rows per expert: prefill). A 256-thread block owns
-//    four 64-row groups x 128 tokens; the gathered activation tile goes
+//    four 64-row groups x 64 tokens; the gathered activation tile goes
 //    through a double-buffered LDS ring (128 K per step), weights straight to
-//    registers as above.
+//    registers as above; blocks are numbered XCD by XCD.
 #include "moe_device.h"
 #include "moe_launch.h"
 

@@ -1,4 +1,5 @@
-// Stable expert permutation of the routed slots (one workgroup), and the
+// Stable expert permutation of the routed slots (one workgroup up to 1024
+// slots, histogram + scan + parallel scatter above), and the
 // weighted combine of per-slot expert outputs.
 #include "moe_block_permute.h"
 #include "moe_device.h"

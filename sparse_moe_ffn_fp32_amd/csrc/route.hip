@@ -16,10 +16,11 @@
 //  * few tokens (T <= 128, T*E <= 4096): the K dimension is cut into 20 chunks, one wave
 //    per (32-token tile, chunk) writes partial logits to scratch; a single
 //    1024-thread block adds the 20 partials in chunk order, adds the bias,
-//    selects the top k and, for the full layer, also builds the expert
-//    permutation (so decoding needs two small launches for all routing).
+//    selects the top k and, when asked, also builds the expert permutation
+//    (two small launches for all routing).
 //  * many tokens: a block per 32 tokens, its waves split K and add their
-//    partial tiles in wave order through LDS, then select the top k.
+//    partial tiles in wave order through LDS, then select the top k and
+//    count the block's routed slots per expert for the parallel permutation.
 #include "moe_block_permute.h"
 #include "moe_device.h"
 #include "moe_launch.h"
