@@ -178,6 +178,25 @@ def test_forward_small(T, E, k):
     assert_out_close(np_(out), ref["out"], "forward")
 
 
+def test_forward_max_experts_and_topk():
+    """E = 256, k = 8 (the largest supported): few tokens through the
+    weight-streaming kernels, and a tiled batch checked on sampled tokens."""
+    for T, E, k, sampled in ((6, 256, 8, False), (800, 256, 8, True)):
+        say(f"forward T={T} E={E} k={k}")
+        inp = make_layer_inputs(T, E, k, seed=4000 + T)
+        d = to_device(inp)
+        ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+        out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=k)
+        torch.cuda.synchronize()
+        ids_h = np_(ids)
+        logits = oracle.router_logits(inp["x"], inp["Wr"], inp["br"])
+        check_routing(ids_h, np_(w), logits, k)
+        tokens = np.array([0, 1, T // 2, T - 1]) if sampled else None
+        ref = oracle.forward(inp, k, tokens=tokens, ids_override=ids_h)
+        got = np_(out)[tokens] if sampled else np_(out)
+        assert_out_close(got, ref["out"], f"E={E} k={k} T={T}")
+
+
 def test_forward_one_expert_takes_all():
     """A dominant router bias sends every token to one expert (others empty)."""
     for T, E, k, hot in ((40, 8, 2, 5), (400, 4, 1, 2)):
