@@ -109,7 +109,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs the layer on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs the layer on one GPU only: the library has no multi-GPU path "
               "(expert-parallel sharding is a design note). Run with --gpus 1.", file=sys.stderr)
         return 2
 

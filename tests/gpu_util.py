@@ -1,5 +1,5 @@
 """Shared helpers of the GPU parity tests: host -> device transfer, the
-spec comparison metrics, and the near-tie rule for routing."""
+acceptance metrics (max error over RMS, mean per-token relative L2), and the near-tie rule for routing."""
 from __future__ import annotations
 
 import numpy as np
