@@ -121,13 +121,6 @@ struct SkStage {
   uint4 xv[4];
 };
 
-// One work item: RG consecutive 64-row groups G0.. of expert e. One wave streams RG groups
-// (64*RG rows: the activations it reads are shared by all of them). The
-// weight stream needs no routing data, so the wave only waits for the
-// expert's row range and its first row lookups before the stream starts; a
-// dependent load issued behind the chip-wide weight traffic would wait for
-// the whole in-flight volume. An expert with more than 16 rows is handled 16
-// at a time.
 // Position of the n-th set bit (n < popcount) of a 64-bit mask.
 __device__ __forceinline__ int nth_set_bit(unsigned long long m, int n) {
   int pos = 0;
@@ -167,6 +160,13 @@ __device__ __forceinline__ void scan_expert_slots(const int32_t* ids, int n, int
   }
 }
 
+// One work item: RG consecutive 64-row groups G0.. of expert e. One wave streams RG groups
+// (64*RG rows: the activations it reads are shared by all of them). The
+// weight stream needs no routing data, so the wave only waits for the
+// expert's row range and its first row lookups before the stream starts; a
+// dependent load issued behind the chip-wide weight traffic would wait for
+// the whole in-flight volume. An expert with more than 16 rows is handled 16
+// at a time.
 template <int EPI, int RG, class WaitAct>
 __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, const WaitAct& wait_act) {
   constexpr int MT = 4 * RG;
