@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec; % HBM BW (decode) / % MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+FP6_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP6 / FP4 matrix cores
 H = I = 2880
 W13_EXPERT_BYTES = 2 * I * H // 2 + 2 * I * H // 32 + 2 * I * 2   # codes + scales + bf16 bias
 W2_EXPERT_BYTES = H * I // 2 + H * I // 32 + H * 2
@@ -102,6 +103,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle sample (0: automatic)")
+    ap.add_argument("--path", choices=("bf16", "mx6"), default="bf16",
+                    help="tiled expert GEMMs on bf16 activations (moe_forward) or on two-piece "
+                         "MX FP6 activations with the block-scaled FP4 matrix cores "
+                         "(moe_forward_mx6)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the bench, run a plain device copy of this size "
                          "(reference kernel for the HBM byte counters)")
@@ -151,10 +156,12 @@ def main() -> int:
     ws = torch.empty(moe.workspace_size(T, E, k), dtype=torch.uint8, device=dev)
     log(f"bench: {copies} weight copies ({copies * layer_bytes / 1e9:.2f} GB)")
 
+    fwd = moe.forward_mx6 if args.path == "mx6" else moe.forward
+
     def step(i):
         w = sets[i % copies]
-        moe.forward(x, w["Wr"], w["br"], w["w13_codes"], w["w13_scales"], w["b13"],
-                    w["w2_codes"], w["w2_scales"], w["b2"], k=k, out=out, workspace=ws)
+        fwd(x, w["Wr"], w["br"], w["w13_codes"], w["w13_scales"], w["b13"],
+            w["w2_codes"], w["w2_scales"], w["b2"], k=k, out=out, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -200,10 +207,15 @@ def main() -> int:
     ids, tw = moe.route(x, w0["Wr"], w0["br"], k=k, workspace=ws)
     counts, offsets, rows = moe.permute(ids, E, workspace=ws)
     h = torch.empty((T * k, I), dtype=torch.int16, device=dev)
+    mx6 = args.path == "mx6" and cfg.regime != "decode"
+    xrec = moe.encode_mx6(x) if mx6 else None
 
     def gate_up(i):
         w = sets[i % copies]
-        moe.gate_up(x, offsets, rows, w["w13_codes"], w["w13_scales"], w["b13"], k=k, h=h)
+        if mx6:
+            moe.gate_up_mx6(xrec, offsets, rows, w["w13_codes"], w["w13_scales"], w["b13"], k=k, h=h)
+        else:
+            moe.gate_up(x, offsets, rows, w["w13_codes"], w["w13_scales"], w["b13"], k=k, h=h)
 
     for i in range(args.warmup):
         gate_up(i)
@@ -231,6 +243,21 @@ def main() -> int:
         layer_alg = touched * (W13_EXPERT_BYTES + W2_EXPERT_BYTES) + E * (H * 4 + 4) \
             + T * H * 2 + T * H * 4 + T * k * 8
         layer_frac = layer_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    elif mx6:
+        # block-scaled FP4 x FP6 matrix cores: two MFMAs per product (one per
+        # activation piece), priced against the FP6/FP4 dense peak
+        alg = 2.0 * T * k * H * 2 * I
+        achieved = alg / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP6_FP4_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP6_FP4_PEAK_TFLOPS, 4),
+                "traffic": None,
+                "kernel": "ffn_wide6_kernel<EPI_SWIGLU> (gate/up + SwiGLU, FP4 x FP6 pieces)",
+                "algorithmic_flop_per_launch": alg,
+                "mfma_flop_issued_per_launch": 2 * alg,
+                "issued_frac": round(2 * achieved / FP6_FP4_PEAK_TFLOPS, 4),
+                "bf16_peak_frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+        layer_flop = 2.0 * T * k * (H * 2 * I + H * I) + 2.0 * T * H * E
+        layer_frac = layer_flop / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
     else:
         alg = 2.0 * T * k * H * 2 * I
         achieved = alg / (kern_ms * 1e-3) / 1e12
@@ -253,7 +280,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp4 x mxfp6 (2 pieces)" if mx6 else "bf16",
         "data": "synthetic",
         "config": {"workload": workload, "T": T, "E": E, "k": k, "hidden": H,
                    "intermediate": I, "weights": "MXFP4 (E2M1 + E8M0 per 32)",

@@ -193,6 +193,60 @@ moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
                          int T, int E, int k, float* out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* The same layer with the tiled (many rows per expert) expert GEMMs on the
+ * block-scaled FP4 matrix cores of CDNA4 (v_mfma_scale_f32_16x16x128_f8f6f4):
+ * the MXFP4 weights enter the instruction as they are (their E8M0 scales are
+ * the instruction's block scales) and each activation row x[t] is held as
+ * two MX FP6 (E2M3) pieces, P1 + P2 (moe_encode_mx6), each multiplied by the
+ * weights at the FP4 x FP6 rate. The pieces stand for x[t] to within
+ * max|x_block| / 256 per 32-value block; the layer output stays within the
+ * accuracy of moe_forward's bf16 matrix-core path while the weight scales of
+ * an expert span up to about 16 binades (checkpoint-like weights span a few);
+ * past that, use moe_forward. The down projection and the
+ * few-rows-per-expert (decode) schedule are those of moe_forward. Arguments,
+ * workspace and errors as moe_forward. Source: the pages fix MXFP4 weights
+ * and their packing for inference (techniques map, "inference & serving");
+ * the piece encoding follows the OCP Microscaling v1.0 conversion and is
+ * this library's. */
+moe_status_t moe_forward_mx6(const uint16_t* x, const float* Wr, const float* br,
+                             const uint8_t* w13_codes, const uint8_t* w13_scales,
+                             const uint16_t* b13,
+                             const uint8_t* w2_codes, const uint8_t* w2_scales,
+                             const uint16_t* b2,
+                             int T, int E, int k, float* out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Two-piece MX FP6 encoding of bf16 activation rows, as moe_forward_mx6 uses it:
+ *   x       [rows, 2880] bf16 (in), 16-byte aligned
+ *   records [rows, 23, 256] u8 (out), 16-byte aligned
+ * 0 <= rows <= MOE_MAX_ROUTED. For each 32-value block V of a row (OCP MX
+ * v1.0 conversion to FP6 E2M3): X = floor(log2(max|V|)) - 2, clamped to
+ * [-127, 127] (0 for an all-zero block); codes = V / 2^X rounded to the
+ * nearest E2M3 value, ties to even, saturating at 7.5; sign bit set for
+ * negative values; scale byte X + 127. Piece 1 encodes V, piece 2 the exact
+ * residual V - piece 1. Record s of a row covers MX blocks 4s .. 4s+3 (blocks
+ * 90, 91 are zero codes with scale byte 127) as sixteen 16-byte chunks:
+ *   0..3   piece 1, block g = 0..3: code bytes 0..15
+ *   4..7   piece 2, the same
+ *   8, 9   piece 1: code bytes 16..23 of blocks 0, 1 (chunk 8) and 2, 3 (chunk 9)
+ *   10, 11 piece 2, the same
+ *   12     scale bytes: byte 2g = piece 1, byte 2g + 1 = piece 2 of block g;
+ *          bytes 8..15 zero
+ *   13..15 zero
+ * Element j of a block sits at bits 6j .. 6j+5 of its 24 code bytes (little
+ * endian). */
+moe_status_t moe_encode_mx6(const uint16_t* x, int rows, uint8_t* records, void* stream);
+
+/* moe_gate_up with the activations given as moe_encode_mx6 records
+ * x_records [T, 23, 256] u8 (16-byte aligned) instead of bf16 rows: the
+ * block-scaled FP4 x FP6 gate/up GEMM of moe_forward_mx6, always in its tiled
+ * schedule. Other arguments, output and errors as moe_gate_up. */
+moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
+                             const int32_t* sorted_rows,
+                             const uint8_t* w13_codes, const uint8_t* w13_scales,
+                             const uint16_t* b13, int T, int E, int k,
+                             uint16_t* h, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status_t status);
 

@@ -21,7 +21,10 @@ H = 2880
 I = 2880
 
 __all__ = ["MoeError", "workspace_size", "pack_weights", "pack_expert_weights", "route", "permute", "expert_ffn", "gate_up",
-           "down_accumulate", "combine", "forward", "H", "I"]
+           "down_accumulate", "combine", "forward", "forward_mx6", "encode_mx6", "gate_up_mx6",
+           "MX6_ROW_BYTES", "H", "I"]
+
+MX6_ROW_BYTES = 5888   # two-piece MX FP6 record bytes per activation row
 
 
 class MoeError(RuntimeError):
@@ -185,6 +188,27 @@ def gate_up(x, offsets, sorted_rows, w13_codes, w13_scales, b13, k: int = 4,
     return h
 
 
+def gate_up_mx6(x_records, offsets, sorted_rows, w13_codes, w13_scales, b13, k: int = 4,
+                h: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gate_up with the activations as encode_mx6 records uint8 [T, 23, 256]."""
+    T = x_records.shape[0]
+    E = w13_codes.shape[0]
+    _dev(x_records, "x_records", _U8, (T, 23, 256))
+    _dev(w13_codes, "w13_codes", _U8, (E, 2 * I, H // 2))
+    _dev(w13_scales, "w13_scales", _U8, (E, 2 * I, H // 32))
+    _dev(b13, "b13", _BF16, (E, 2 * I))
+    _dev(offsets, "offsets", _I32, (E + 1,))
+    _dev(sorted_rows, "sorted_rows", _I32, (T * k,))
+    if h is None:
+        h = torch.empty((T * k, I), dtype=torch.int16, device=x_records.device)
+    else:
+        _dev(h, "h", _BF16, (T * k, I))
+    _check(_native.lib().moe_gate_up_mx6(
+        _ptr(x_records), _ptr(offsets), _ptr(sorted_rows), _ptr(w13_codes), _ptr(w13_scales),
+        _ptr(b13), T, E, k, _ptr(h), _stream(x_records)), "moe_gate_up_mx6")
+    return h
+
+
 def down_accumulate(h, offsets, sorted_rows, topk_w, w2_codes, w2_scales, b2,
                     out: torch.Tensor, k: int = 4) -> torch.Tensor:
     """out[t] += sum_j topk_w[t, j] * (W2[e] h + b2[e]) over the slots of t; returns out."""
@@ -219,6 +243,30 @@ def forward(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, k: i
             out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole layer -> out fp32 [T, 2880]."""
+    return _forward("moe_forward", x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales,
+                    b2, k, out, workspace)
+
+
+def forward_mx6(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, k: int = 4,
+                out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole layer with the tiled expert GEMMs on the block-scaled FP4 x FP6
+    matrix cores (activations as two MX FP6 pieces) -> out fp32 [T, 2880]."""
+    return _forward("moe_forward_mx6", x, Wr, br, w13_codes, w13_scales, b13, w2_codes,
+                    w2_scales, b2, k, out, workspace)
+
+
+def encode_mx6(x: torch.Tensor) -> torch.Tensor:
+    """bf16 rows [R, 2880] -> two-piece MX FP6 records uint8 [R, 23, 256]."""
+    R = x.shape[0]
+    _dev(x, "x", _BF16, (R, H))
+    rec = torch.empty((R, 23, 256), dtype=torch.uint8, device=x.device)
+    _check(_native.lib().moe_encode_mx6(_ptr(x), R, _ptr(rec), _stream(x)), "moe_encode_mx6")
+    return rec
+
+
+def _forward(fn, x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, k, out,
+             workspace) -> torch.Tensor:
     T = x.shape[0]
     E = Wr.shape[0]
     _dev(x, "x", _BF16, (T, H))
@@ -231,8 +279,8 @@ def forward(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, k: i
     else:
         _dev(out, "out", _F32, (T, H))
     ws = _workspace(T, E, k, x.device, workspace)
-    _check(_native.lib().moe_forward(
+    _check(getattr(_native.lib(), fn)(
         _ptr(x), _ptr(Wr), _ptr(br), _ptr(w13_codes), _ptr(w13_scales), _ptr(b13),
         _ptr(w2_codes), _ptr(w2_scales), _ptr(b2), T, E, k, _ptr(out), _ptr(ws), ws.numel(),
-        _stream(x)), "moe_forward")
+        _stream(x)), fn)
     return out

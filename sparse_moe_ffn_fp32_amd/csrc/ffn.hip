@@ -349,7 +349,27 @@ constexpr int kXRow = 256;     // bytes per token row of an LDS activation stage
 constexpr int kXStage = kWdBT * kXRow;   // 16 KiB
 constexpr int kXLoads = kWdBT / 16;   // 1 KiB LDS DMA instructions per wave per stage
 
-// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
+// One lane's FP6 activation operand from an LDS stage of MX6 records (record
+// layout in moe_device.h; 16-byte pieces swizzled by token & 15 like the bf16
+// rows): the 24 code bytes of MX block g of one piece for token 16 nt + r.
+struct X6Half {
+  uint4 lo;
+  uint2 hi;
+  __device__ __forceinline__ void read(const uint8_t* xsb, int nt, int piece, int r, int g) {
+    const uint8_t* xr = xsb + (16 * nt + r) * kXRow;
+    lo = *reinterpret_cast<const uint4*>(xr + ((4 * piece + g) ^ r) * 16);
+    hi = *reinterpret_cast<const uint2*>(xr + ((8 + 2 * piece + (g >> 1)) ^ r) * 16 + (g & 1) * 8);
+  }
+  // both pieces' scale bytes of block g (piece 1 in bits 0..7, piece 2 in 8..15)
+  __device__ __forceinline__ static uint32_t read_scales(const uint8_t* xsb, int nt, int r, int g) {
+    return *reinterpret_cast<const uint16_t*>(xsb + (16 * nt + r) * kXRow + (12 ^ r) * 16 + 2 * g);
+  }
+  __device__ __forceinline__ i32x8 operand() const {
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, 0, 0};
+  }
+};
+
+// s_waitcnt with only a vmcnt limit// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -364,8 +384,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // fragment load hit distinct banks. Weights stream to registers (2-step
 // ring) as in the skinny kernel. Per K step: wait for this step's loads,
 // barrier, issue the next activation stage, compute, refill the weights.
-template <int EPI, bool W_AS_B>
-__global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
+template <int EPI, bool W_AS_B, bool MX6>
+__device__ __forceinline__ void wide_body(const FfnArgs& a) {
   __shared__ __attribute__((aligned(1024))) uint8_t xs[2 * kXStage];
   __shared__ int slot_of[kWdBT];
   __shared__ uint16_t bias_s[kWdGroups * 64];
@@ -396,25 +416,31 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
   // q = i & 15, which holds K piece q ^ (t & 15). Padded tokens read the
   // tile's first row (outputs dropped); the K tail re-reads the row's last
   // piece (weights zero there), so all LDS values are finite.
+  // With MX6 the rows are two-piece FP6 records instead (256 bytes per K
+  // step, complete, so no tail handling); the same swizzle applies.
   const int q_lds = lane & 15;
-  const uint16_t* xsrc[kXLoads];
+  const uint8_t* xbase = MX6 ? a.act6 : reinterpret_cast<const uint8_t*>(a.act);
+  size_t xoff[kXLoads];
   int xpiece[kXLoads];
 #pragma unroll
   for (int j = 0; j < kXLoads; ++j) {
     const int t = 4 * (kXLoads * wave + j) + (lane >> 4);
     const int p = rb + t < re ? rb + t : rb;
     const int row = a.gather ? a.sorted_rows[p] / a.k : p;
-    xsrc[j] = a.act + (size_t)row * kH;
     xpiece[j] = q_lds ^ (t & 15);
+    xoff[j] = MX6 ? (size_t)row * kRowRecBytes + xpiece[j] * 16 : (size_t)row * (2 * kH);
   }
-  auto load_x = [&](int s, int stage) __attribute__((always_inline)) {
+  auto load_x = [&](uint8_t* dst, int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j) {
-      const int off = min(s * 128 + xpiece[j] * 8, kH - 8);
+      const uint8_t* src;
+      if constexpr (MX6)
+        src = xbase + xoff[j] + s * kRecBytes;
+      else
+        src = xbase + xoff[j] + 2 * min(s * 128 + xpiece[j] * 8, kH - 8);
       __builtin_amdgcn_global_load_lds(
-          (const void*)(xsrc[j] + off),
-          (__attribute__((address_space(3))) void*)(xs + stage * kXStage + (kXLoads * wave + j) * 1024),
-          16, 0, 0);
+          (const void*)src,
+          (__attribute__((address_space(3))) void*)(dst + (kXLoads * wave + j) * 1024), 16, 0, 0);
     }
   };
 
@@ -431,8 +457,51 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
 #pragma unroll
     for (int nt = 0; nt < kWdNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int stage, int buf) __attribute__((always_inline)) {
-    const uint8_t* xsb = xs + stage * kXStage;
+  auto compute = [&](const uint8_t* xsb, int buf) __attribute__((always_inline)) {
+    if constexpr (MX6) {
+      // Block-scaled FP4 x FP6 (16x16x128): the packed weight lane holds one
+      // whole MX block, which is the instruction's operand as it stands; its
+      // scale is byte mt of the step's scale dword (the instruction reads
+      // byte 0 of the scale operand). Two MFMAs per tile pair, one per piece.
+      // One (token tile, piece) operand is read from LDS while the previous
+      // one computes; scheduling barriers and register-tied empty asm keep
+      // that order (otherwise every tile's operands are loaded up front and
+      // the registers of three waves per SIMD overflow).
+      int wsa[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) wsa[mt] = (int)(wsc[buf] >> (8 * mt));
+      X6Half hb[2];
+      uint32_t scb[2];
+      hb[0].read(xsb, 0, 0, r, g);
+      scb[0] = X6Half::read_scales(xsb, 0, r, g);
+#pragma unroll
+      for (int q = 0; q < 2 * kWdNT; ++q) {
+        const int nt = q >> 1, piece = q & 1;
+        if (q + 1 < 2 * kWdNT) {
+          hb[(q + 1) & 1].read(xsb, (q + 1) >> 1, (q + 1) & 1, r, g);
+          if (((q + 1) & 1) == 0) scb[((q + 1) >> 1) & 1] = X6Half::read_scales(xsb, (q + 1) >> 1, r, g);
+        }
+        asm volatile("" ::: "memory");   // no LDS read moves across operands
+        __builtin_amdgcn_sched_barrier(0);
+        const i32x8 xp = hb[q & 1].operand();
+        const int xsc = (int)(scb[nt & 1] >> (8 * piece));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const uint4 wv = wq[buf][mt];
+          const i32x8 wa = {(int)wv.x, (int)wv.y, (int)wv.z, (int)wv.w, 0, 0, 0, 0};
+          if constexpr (W_AS_B)
+            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                xp, wa, acc[mt][nt], kFmtE2M3, kFmtFp4, 0, xsc, 0, wsa[mt]);
+          else
+            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                wa, xp, acc[mt][nt], kFmtFp4, kFmtE2M3, 0, wsa[mt], 0, xsc);
+        }
+        // pins this operand's matrix-core work before the next LDS reads
+        asm volatile("" : "+v"(acc[0][nt]), "+v"(acc[1][nt]), "+v"(acc[2][nt]), "+v"(acc[3][nt]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
     float sf[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) sf[mt] = e8m0_to_f32((wsc[buf] >> (8 * mt)) & 0xFFu);
@@ -466,7 +535,7 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
     wsrc.load(0, wq[0], wsc[0]);
     wsrc.load(1, wq[1], wsc[1]);
   }
-  load_x(0, 0);
+  load_x(xs, 0);
   for (int s0 = 0; s0 < kSteps; s0 += 2) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -475,9 +544,9 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
         if (s == 0 || !w_ok || s + 1 >= kSteps) wait_vmcnt<0>();
         else wait_vmcnt<5>();
         __builtin_amdgcn_s_barrier();
-        if (s + 1 < kSteps) load_x(s + 1, q ^ 1);
+        if (s + 1 < kSteps) load_x(xs + (q ^ 1) * kXStage, s + 1);
         if (w_ok) {
-          compute(q, q);
+          compute(xs + q * kXStage, q);
           if (s + 2 < kSteps) wsrc.load(s + 2, wq[q], wsc[q]);
         }
       }
@@ -528,6 +597,19 @@ __global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
   }
 }
 
+template <int EPI, bool W_AS_B>
+__global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
+  wide_body<EPI, W_AS_B, false>(a);
+}
+
+// The FP6 fragments of four token tiles would otherwise all be loaded ahead
+// of the matrix-core work, leaving room for two waves per SIMD; three keep
+// the load latency covered.
+template <int EPI, bool W_AS_B>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void ffn_wide6_kernel(FfnArgs a) {
+  wide_body<EPI, W_AS_B, true>(a);
+}
+
 // ------------------------------------------------------------------ dispatch
 constexpr int kSkinnyMaxMeanRows = 24;
 
@@ -537,7 +619,7 @@ bool ffn_uses_tiles(int n_rows, int E) {
 
 hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s) {
   const int groups = a.N >> 6;
-  const bool skinny = !ffn_uses_tiles(n_rows, a.E);
+  const bool skinny = !a.act6 && !ffn_uses_tiles(n_rows, a.E);   // records: tiled only
   if (skinny) {
     switch (epi) {
       case EPI_SWIGLU: launch_skinny<EPI_SWIGLU>(a, s); break;
@@ -547,6 +629,14 @@ hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s)
   } else {
     const int tiles = (n_rows + kWdBT - 1) / kWdBT + min(a.E, n_rows);
     const dim3 grid(((groups + kWdGroups - 1) / kWdGroups) * tiles);
+    if (a.act6) {
+      switch (epi) {
+        case EPI_SWIGLU: hipLaunchKernelGGL((ffn_wide6_kernel<EPI_SWIGLU, false>), grid, dim3(256), 0, s, a); break;
+        case EPI_COMBINE: hipLaunchKernelGGL((ffn_wide6_kernel<EPI_COMBINE, true>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((ffn_wide6_kernel<EPI_STORE_Y, true>), grid, dim3(256), 0, s, a); break;
+      }
+      return hipGetLastError();
+    }
     switch (epi) {
       case EPI_SWIGLU: hipLaunchKernelGGL((ffn_wide_kernel<EPI_SWIGLU, false>), grid, dim3(256), 0, s, a); break;
       case EPI_COMBINE: hipLaunchKernelGGL((ffn_wide_kernel<EPI_COMBINE, true>), grid, dim3(256), 0, s, a); break;

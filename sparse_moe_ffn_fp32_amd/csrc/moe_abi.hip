@@ -21,7 +21,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t ids, w, counts, offsets, sorted, scratch, h, y, total;
+  size_t ids, w, counts, offsets, sorted, scratch, h, y, xrec, total;
 };
 
 bool sizes_ok(int T, int E, int k) {
@@ -43,7 +43,11 @@ WsLayout layout(int T, int E, int k) {
   // per-slot fp32 expert outputs: the many-rows schedule stores them and sums
   // a token's k rows in a second pass instead of atomically adding into out
   l.y = off;
-  if (n > 0 && moe::ffn_uses_tiles((int)n, E)) off = align_up(off + n * (size_t)moe::kH * 4);
+  const bool tiles = n > 0 && moe::ffn_uses_tiles((int)n, E);
+  if (tiles) off = align_up(off + n * (size_t)moe::kH * 4);
+  // the tiled schedule of moe_forward_mx6: x as two-piece MX FP6 records
+  l.xrec = off;
+  if (tiles) off = align_up(off + (size_t)T * moe::kRowRecBytes);
   l.total = off;
   return l;
 }
@@ -230,6 +234,26 @@ moe_status_t moe_gate_up(const uint16_t* x, const int32_t* offsets, const int32_
   return after_launch(moe::launch_ffn(a, moe::EPI_SWIGLU, T * k, s), s);
 }
 
+moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
+                             const int32_t* sorted_rows, const uint8_t* w13_codes,
+                             const uint8_t* w13_scales, const uint16_t* b13, int T, int E, int k,
+                             uint16_t* h, void* stream) {
+  if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x_records || !offsets || !sorted_rows || !w13_codes || !w13_scales || !b13 || !h)
+    return MOE_ERROR_INVALID_VALUE;
+  if (!aligned(x_records, 16) || !aligned(h, 16) || !aligned(w13_codes, 16) ||
+      !aligned(w13_scales, 4) || !aligned(b13, 8) || !aligned(offsets, 4) ||
+      !aligned(sorted_rows, 4))
+    return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FfnArgs a = ffn_args(nullptr, offsets, sorted_rows, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
+  a.act6 = x_records;
+  a.h_out = h;
+  return after_launch(moe::launch_ffn(a, moe::EPI_SWIGLU, T * k, s), s);
+}
+
 moe_status_t moe_down_accumulate(const uint16_t* h, const int32_t* offsets,
                                  const int32_t* sorted_rows, const float* topk_w,
                                  const uint8_t* w2_codes, const uint8_t* w2_scales,
@@ -262,10 +286,15 @@ moe_status_t moe_combine(const float* y, const float* topk_w, int T, int k, floa
   return after_launch(moe::launch_combine(y, topk_w, T, k, out, s), s);
 }
 
-moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
-                         const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
-                         const uint8_t* w2_codes, const uint8_t* w2_scales, const uint16_t* b2,
-                         int T, int E, int k, float* out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status_t forward_impl(const uint16_t* x, const float* Wr, const float* br,
+                          const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
+                          const uint8_t* w2_codes, const uint8_t* w2_scales, const uint16_t* b2,
+                          int T, int E, int k, float* out, void* ws, size_t ws_bytes, void* stream,
+                          bool mx6) {
   if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
   if (T == 0) return MOE_SUCCESS;
   if (!x || !Wr || !br || !out) return MOE_ERROR_INVALID_VALUE;
@@ -296,6 +325,10 @@ moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
   if (!tiles) {
     a13.ids = ids;
     a13.n_slots = n;
+  } else if (mx6) {
+    uint8_t* xrec = reinterpret_cast<uint8_t*>(base + l.xrec);
+    MOE_TRY(after_launch(moe::launch_mx6_encode(x, T, xrec, s), s));
+    a13.act6 = xrec;
   }
   MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));
   FfnArgs a2 = ffn_args(h, offsets, sorted, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
@@ -312,6 +345,37 @@ moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
   a2.y_out = y;
   MOE_TRY(after_launch(moe::launch_ffn(a2, moe::EPI_STORE_Y, n, s), s));
   return after_launch(moe::launch_combine(y, w, T, k, out, s), s);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
+                         const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
+                         const uint8_t* w2_codes, const uint8_t* w2_scales, const uint16_t* b2,
+                         int T, int E, int k, float* out, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, E, k, out,
+                      ws, ws_bytes, stream, false);
+}
+
+moe_status_t moe_forward_mx6(const uint16_t* x, const float* Wr, const float* br,
+                             const uint8_t* w13_codes, const uint8_t* w13_scales,
+                             const uint16_t* b13, const uint8_t* w2_codes,
+                             const uint8_t* w2_scales, const uint16_t* b2, int T, int E, int k,
+                             float* out, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, E, k, out,
+                      ws, ws_bytes, stream, true);
+}
+
+moe_status_t moe_encode_mx6(const uint16_t* x, int rows, uint8_t* records, void* stream) {
+  if (rows < 0 || rows > MOE_MAX_ROUTED) return MOE_ERROR_INVALID_VALUE;
+  if (rows == 0) return MOE_SUCCESS;
+  if (!x || !records) return MOE_ERROR_INVALID_VALUE;
+  if (!aligned(x, 16) || !aligned(records, 16)) return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(moe::launch_mx6_encode(x, rows, records, s), s);
 }
 
 }  // extern "C"

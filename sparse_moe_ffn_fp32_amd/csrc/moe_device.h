@@ -27,10 +27,30 @@ constexpr int kStepCodeBytes = 4096;     // four tiles x 1 KiB
 constexpr int kGroupCodeBytes = 64 * kRowCodeBytes;    // 92,160
 constexpr int kGroupScaleBytes = 64 * kRowScaleBytes;  // 5,760
 
+// Two-piece MX FP6 activation records (the block-scaled matrix-core path):
+// an activation row v is held as P1 + P2, P1 the MX E2M3 encoding of v and
+// P2 that of the exact residual v - P1 (OCP MX v1.0 conversion: shared
+// exponent floor(log2(amax)) - 2, round to nearest even, saturate at 7.5).
+// Per row, one 256-byte record per K step s of four MX blocks (blocks 90, 91
+// of the last step are zero codes with scale 2^0). A record is sixteen
+// 16-byte pieces: 0..3 = piece 1 code bytes 0..15 of block g; 4..7 = piece 2
+// the same; 8, 9 = piece 1 code bytes 16..23 of blocks (0, 1) and (2, 3);
+// 10, 11 = piece 2 the same; 12 = scale bytes, byte 2g + p for piece p of
+// block g, then 8 zero bytes; 13..15 = zero. Element j of a block sits at
+// bits 6j..6j+5 of its 24 code bytes (little endian), the operand order of
+// the f8f6f4 matrix-core instructions.
+constexpr int kRecBytes = 256;
+constexpr int kRowRecBytes = kSteps * kRecBytes;   // 5,888 per activation row
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// operand format codes of the f8f6f4 matrix-core instructions
+constexpr int kFmtE2M3 = 2;
+constexpr int kFmtFp4 = 4;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
@@ -122,6 +142,62 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   row_end = base + min(n, (t_in + 1) * bt);
   (void)cnt;
   return true;
+}
+
+// ------------------------------------------------- MX FP6 (E2M3) encoding
+// Shared exponent of a block with largest magnitude amax: floor(log2(amax))
+// - 2 (emax of E2M3), clamped to the E8M0 range; 0 for an all-zero block.
+__device__ __forceinline__ int mx6_shared_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const int X = __builtin_amdgcn_frexp_expf(amax) - 3;   // amax = f * 2^e, f in [0.5, 1)
+  return min(max(X, -127), 127);
+}
+
+// E2M3 magnitude code nearest to a >= 0 (ties to the even code, saturating
+// at 7.5) and its value q. Within the binade [2^e, 2^(e+1)) (e = 0 also
+// covers the subnormals) the grid step is 2^(e-3), so the code is 8e plus
+// the rounded multiple of the step; a carry into the next binade lands on
+// the right code because codes count up through the binades.
+__device__ __forceinline__ uint32_t e2m3_mag_code(float a, float& q) {
+  a = fminf(a, 7.5f);
+  const int e = a >= 4.f ? 2 : (a >= 2.f ? 1 : 0);
+  const float n = rintf(ldexpf(a, 3 - e));
+  q = ldexpf(n, e - 3);
+  return 8u * (uint32_t)e + (uint32_t)n;
+}
+
+// One MX E2M3 piece of 32 values: codes packed 6 bits each (element j at
+// bits 6j) into w[0..5], the scale byte, and the exact residual v - piece.
+__device__ __forceinline__ void mx6_encode_piece(const float (&v)[32], uint32_t (&w)[6],
+                                                 uint32_t& scale, float (&res)[32]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const int X = mx6_shared_exp(amax);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) w[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    float q;
+    uint32_t c = e2m3_mag_code(ldexpf(fabsf(v[j]), -X), q);
+    if (v[j] < 0.f) {
+      c |= 32u;
+      q = -q;
+    }
+    res[j] = v[j] - ldexpf(q, X);
+    const int bit = 6 * j, word = bit >> 5, off = bit & 31;
+    w[word] |= c << off;
+    if (off > 26) w[word + 1] |= c >> (32 - off);
+  }
+  scale = (uint32_t)(X + 127);
+}
+
+// Both pieces of a 32-value block.
+__device__ __forceinline__ void mx6x2_encode(const float (&v)[32], uint32_t (&w1)[6], uint32_t& s1,
+                                             uint32_t (&w2)[6], uint32_t& s2) {
+  float r1[32], r2[32];
+  mx6_encode_piece(v, w1, s1, r1);
+  mx6_encode_piece(r1, w2, s2, r2);
 }
 
 }  // namespace moe

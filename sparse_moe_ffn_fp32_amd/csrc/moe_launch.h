@@ -32,6 +32,10 @@ struct FfnArgs {
   // positions as the permutation) and offsets / sorted_rows are not read.
   const int32_t* ids;
   int n_slots;
+  // Tiled kernels only: when not null, the activations are read from these
+  // two-piece MX FP6 records ([rows, 23 steps, 256 B], moe_device.h) through
+  // the block-scaled FP4 x FP6 matrix-core instruction instead of `act`.
+  const uint8_t* act6;
 };
 
 // Router + top-k + softmax. `zero_out` (optional) is cleared for the
@@ -62,6 +66,9 @@ hipError_t launch_permute_blocks(const int32_t* ids, int n, int E, int32_t* hist
 // grouped GEMM from the mean rows per expert, n_rows / E.
 hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s);
 bool ffn_uses_tiles(int n_rows, int E);
+
+// bf16 rows [rows, 2880] -> two-piece MX FP6 records [rows, 23, 256 B]
+hipError_t launch_mx6_encode(const uint16_t* x, int rows, uint8_t* rec, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const float* w, int T, int k, float* out, hipStream_t s);
 

@@ -21,7 +21,7 @@ P = ctypes.c_void_p
 def header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -161,3 +161,47 @@ def test_forward_validation(L):
     assert fwd(L, Wr=A + 4) == MISALIGNED
     assert fwd(L, ws=None) == WORKSPACE
     assert fwd(L, nbytes=L.moe_workspace_size(4, 32, 4) - 1) == WORKSPACE
+
+
+def test_forward_mx6_validation(L):
+    def f(T=4, E=32, k=4, x=A, out=A, ws=A, nbytes=None, c13=A):
+        if nbytes is None:
+            nbytes = L.moe_workspace_size(max(T, 0), E, k)
+        return L.moe_forward_mx6(P(x), P(A), P(A), P(c13), P(A), P(A), P(A), P(A), P(A),
+                                 T, E, k, P(out), P(ws), nbytes, None)
+    assert f(T=0) == OK
+    assert f(T=0, x=None, out=None, ws=None) == OK
+    assert f(T=-1) == INVALID
+    assert f(k=9) == INVALID
+    assert f(x=None) == INVALID
+    assert f(c13=None) == INVALID
+    assert f(out=A + 8) == MISALIGNED
+    assert f(ws=None) == WORKSPACE
+    # the tiled schedule also holds the activation records in the workspace
+    T, E, k = 4096, 32, 4
+    assert f(T=T, E=E, k=k, nbytes=L.moe_workspace_size(T, E, k) - 1) == WORKSPACE
+    assert L.moe_workspace_size(T, E, k) >= T * 5888 + T * k * 2880 * 6
+
+
+def test_encode_mx6_validation(L):
+    enc = lambda rows=4, x=A, rec=A: L.moe_encode_mx6(P(x), rows, P(rec), None)
+    assert enc(rows=0) == OK
+    assert enc(rows=0, x=None, rec=None) == OK
+    assert enc(rows=-1) == INVALID
+    assert enc(rows=(1 << 22) + 1) == INVALID
+    assert enc(x=None) == INVALID
+    assert enc(rec=None) == INVALID
+    assert enc(x=A + 8) == MISALIGNED
+    assert enc(rec=A + 4) == MISALIGNED
+
+
+def test_gate_up_mx6_validation(L):
+    g = lambda T=4, E=32, k=4, xr=A, off=A, rows=A, c=A, s=A, b=A, h=A: L.moe_gate_up_mx6(
+        P(xr), P(off), P(rows), P(c), P(s), P(b), T, E, k, P(h), None)
+    assert g(T=0) == OK
+    assert g(T=-1) == INVALID
+    assert g(xr=None) == INVALID
+    assert g(h=None) == INVALID
+    assert g(xr=A + 8) == MISALIGNED
+    assert g(s=A + 2) == MISALIGNED
+    assert g(b=A + 4) == MISALIGNED
