@@ -107,6 +107,9 @@ def main() -> int:
                     help="tiled expert GEMMs on bf16 activations (moe_forward) or on two-piece "
                          "MX FP6 activations with the block-scaled FP4 matrix cores "
                          "(moe_forward_mx6)")
+    ap.add_argument("--block", action="store_true",
+                    help="time the decoder sublayer x + layer(RMSNorm(x)) (moe_forward_block) "
+                         "instead of the layer alone")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the bench, run a plain device copy of this size "
                          "(reference kernel for the HBM byte counters)")
@@ -157,9 +160,17 @@ def main() -> int:
     log(f"bench: {copies} weight copies ({copies * layer_bytes / 1e9:.2f} GB)")
 
     fwd = moe.forward_mx6 if args.path == "mx6" else moe.forward
+    if args.block and args.path == "mx6":
+        print("--block runs the bf16 path (moe_forward_block)", file=sys.stderr)
+        return 2
+    gnorm = torch.ones(H, dtype=torch.float32, device=dev)
 
     def step(i):
         w = sets[i % copies]
+        if args.block:
+            moe.forward_block(x, gnorm, w["Wr"], w["br"], w["w13_codes"], w["w13_scales"], w["b13"],
+                              w["w2_codes"], w["w2_scales"], w["b2"], k=k, out=out, workspace=ws)
+            return
         fwd(x, w["Wr"], w["br"], w["w13_codes"], w["w13_scales"], w["b13"],
             w["w2_codes"], w["w2_scales"], w["b2"], k=k, out=out, workspace=ws)
 
@@ -231,7 +242,7 @@ def main() -> int:
     touched = int((counts > 0).sum().item())
     log(f"bench: gate/up kernel {kern_ms * 1e3:.1f} us per launch, {touched} experts touched")
 
-    workload = f"{cfg.name} (E={E}, k={k})"
+    workload = f"{cfg.name} (E={E}, k={k})" + (" + RMSNorm + residual" if args.block else "")
     if cfg.regime == "decode":
         alg = touched * W13_EXPERT_BYTES + T * H * 2 + T * k * I * 2
         achieved = alg / (kern_ms * 1e-3) / 1e9

@@ -247,6 +247,36 @@ moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
                              const uint16_t* b13, int T, int E, int k,
                              uint16_t* h, void* stream);
 
+/* The MoE sublayer of a gpt-oss decoder layer with its neighbours: the
+ * pre-MoE RMSNorm and the residual add.
+ *   t   = bf16( x / sqrt(mean_h(x^2) + norm_eps) * norm_scale )   per token
+ *   out = x + layer(t)          (layer = moe_forward on t, same kernels)
+ *   x          [T, 2880] bf16, the residual stream entering the sublayer
+ *   norm_scale [2880] fp32 (16-byte aligned); norm_eps >= 0 (gpt-oss: 1e-5)
+ *   out        [T, 2880] fp32 (overwritten)
+ * Other arguments, workspace and errors as moe_forward. Sources: the
+ * "gpt-oss-20b" page, "Structure" table (every layer runs RMSNorm_i_2 ->
+ * MoE_i -> Add_i_ffn); techniques map, "normalization & residual" (RMSNorm,
+ * Pre-LN); rms_norm_eps from the raw config.json tables. Readings: the norm
+ * is computed in fp32 and its output rounded to bf16 (the layer's input
+ * type); the residual is added in fp32. */
+moe_status_t moe_forward_block(const uint16_t* x, const float* norm_scale, float norm_eps,
+                               const float* Wr, const float* br,
+                               const uint8_t* w13_codes, const uint8_t* w13_scales,
+                               const uint16_t* b13,
+                               const uint8_t* w2_codes, const uint8_t* w2_scales,
+                               const uint16_t* b2,
+                               int T, int E, int k, float* out,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* The RMSNorm of moe_forward_block alone:
+ *   t[r, :] = bf16( x[r, :] / sqrt(mean(x[r, :]^2) + eps) * scale )
+ *   x [T, 2880] bf16, t [T, 2880] bf16 (out), both 16-byte aligned;
+ *   scale [2880] fp32, 16-byte aligned; eps >= 0; 0 <= T <= MOE_MAX_ROUTED.
+ * Source as moe_forward_block. */
+moe_status_t moe_rmsnorm(const uint16_t* x, const float* scale, float eps, int T,
+                         uint16_t* t, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status_t status);
 

@@ -21,7 +21,7 @@ H = 2880
 I = 2880
 
 __all__ = ["MoeError", "workspace_size", "pack_weights", "pack_expert_weights", "route", "permute", "expert_ffn", "gate_up",
-           "down_accumulate", "combine", "forward", "forward_mx6", "encode_mx6", "gate_up_mx6",
+           "down_accumulate", "combine", "forward", "forward_mx6", "encode_mx6", "gate_up_mx6", "forward_block", "rmsnorm",
            "MX6_ROW_BYTES", "H", "I"]
 
 MX6_ROW_BYTES = 5888   # two-piece MX FP6 record bytes per activation row
@@ -263,6 +263,42 @@ def encode_mx6(x: torch.Tensor) -> torch.Tensor:
     rec = torch.empty((R, 23, 256), dtype=torch.uint8, device=x.device)
     _check(_native.lib().moe_encode_mx6(_ptr(x), R, _ptr(rec), _stream(x)), "moe_encode_mx6")
     return rec
+
+
+def rmsnorm(x: torch.Tensor, scale: torch.Tensor, eps: float = 1e-5) -> torch.Tensor:
+    """bf16 rows [T, 2880] -> bf16(x / sqrt(mean(x^2) + eps) * scale), as int16 bits."""
+    T = x.shape[0]
+    _dev(x, "x", _BF16, (T, H))
+    _dev(scale, "scale", _F32, (H,))
+    t = torch.empty((T, H), dtype=torch.int16, device=x.device)
+    _check(_native.lib().moe_rmsnorm(_ptr(x), _ptr(scale), float(eps), T, _ptr(t), _stream(x)),
+           "moe_rmsnorm")
+    return t
+
+
+def forward_block(x, norm_scale, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                  k: int = 4, norm_eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out fp32 [T, 2880] = x + layer(bf16(RMSNorm(x))): the MoE sublayer of a
+    decoder layer with its pre-norm and residual add."""
+    T = x.shape[0]
+    E = Wr.shape[0]
+    _dev(x, "x", _BF16, (T, H))
+    _dev(norm_scale, "norm_scale", _F32, (H,))
+    _dev(Wr, "Wr", _F32, (E, H))
+    _dev(br, "br", _F32, (E,))
+    if _weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2) != E:
+        raise ValueError("router and expert weights disagree on the expert count")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    else:
+        _dev(out, "out", _F32, (T, H))
+    ws = _workspace(T, E, k, x.device, workspace)
+    _check(_native.lib().moe_forward_block(
+        _ptr(x), _ptr(norm_scale), float(norm_eps), _ptr(Wr), _ptr(br), _ptr(w13_codes),
+        _ptr(w13_scales), _ptr(b13), _ptr(w2_codes), _ptr(w2_scales), _ptr(b2), T, E, k,
+        _ptr(out), _ptr(ws), ws.numel(), _stream(x)), "moe_forward_block")
+    return out
 
 
 def _forward(fn, x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, k, out,

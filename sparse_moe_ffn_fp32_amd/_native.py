@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libmoe_mi355x.so")
 # every symbol declared in include/moe.h
 EXPORTED = ("moe_workspace_size", "moe_pack_weights", "moe_route", "moe_permute", "moe_expert_ffn",
             "moe_gate_up", "moe_down_accumulate", "moe_combine", "moe_forward",
-            "moe_forward_mx6", "moe_encode_mx6", "moe_gate_up_mx6", "moe_status_string")
+            "moe_forward_mx6", "moe_encode_mx6", "moe_gate_up_mx6", "moe_forward_block",
+            "moe_rmsnorm", "moe_status_string")
 
 MOE_SUCCESS = 0
 STATUS_NAMES = {
@@ -69,5 +70,10 @@ def lib() -> ctypes.CDLL:
     L.moe_encode_mx6.restype = ST
     L.moe_gate_up_mx6.argtypes = [P, P, P, P, P, P, I, I, I, P, P]
     L.moe_gate_up_mx6.restype = ST
+    F = ctypes.c_float
+    L.moe_forward_block.argtypes = [P, P, F, P, P, P, P, P, P, P, P, I, I, I, P, P, SZ, P]
+    L.moe_forward_block.restype = ST
+    L.moe_rmsnorm.argtypes = [P, P, F, I, P, P]
+    L.moe_rmsnorm.restype = ST
     _lib = L
     return L

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["route.hip", "permute.hip", "ffn.hip", "mx6.hip", "moe_abi.hip"]
+SOURCES = ["route.hip", "permute.hip", "ffn.hip", "mx6.hip", "norm.hip", "moe_abi.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -21,7 +21,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t ids, w, counts, offsets, sorted, scratch, h, y, xrec, total;
+  size_t ids, w, counts, offsets, sorted, scratch, h, y, xrec, xnorm, total;
 };
 
 bool sizes_ok(int T, int E, int k) {
@@ -48,6 +48,8 @@ WsLayout layout(int T, int E, int k) {
   // the tiled schedule of moe_forward_mx6: x as two-piece MX FP6 records
   l.xrec = off;
   if (tiles) off = align_up(off + (size_t)T * moe::kRowRecBytes);
+  // moe_forward_block: the normed bf16 input of the layer
+  l.xnorm = off;    off = align_up(off + (size_t)T * moe::kH * 2);
   l.total = off;
   return l;
 }
@@ -161,7 +163,7 @@ moe_status_t moe_route(const uint16_t* x, const float* Wr, const float* br, int 
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* scratch = reinterpret_cast<float*>(static_cast<char*>(ws) + layout(T, E, k).scratch);
-  return after_launch(moe::launch_route(x, Wr, br, T, E, k, topk_ids, topk_w, logits, nullptr,
+  return after_launch(moe::launch_route(x, Wr, br, T, E, k, topk_ids, topk_w, logits, moe::OutInit{nullptr, nullptr},
                                         scratch, nullptr, nullptr, nullptr, s), s);
 }
 
@@ -283,12 +285,20 @@ moe_status_t moe_combine(const float* y, const float* topk_w, int T, int k, floa
   if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_w, 4)) return MOE_ERROR_MISALIGNED;
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(moe::launch_combine(y, topk_w, T, k, out, s), s);
+  return after_launch(moe::launch_combine(y, topk_w, T, k, nullptr, out, s), s);
 }
 
 }  // extern "C"
 
 namespace {
+
+// The layer on x; with `resid` (bf16 [T, 2880]) the output is resid + layer.
+// Arguments are validated by the caller.
+moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
+                            const uint8_t* w13_codes, const uint8_t* w13_scales,
+                            const uint16_t* b13, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                            const uint16_t* b2, int T, int E, int k, float* out, void* ws,
+                            hipStream_t s, bool mx6, const uint16_t* resid);
 
 moe_status_t forward_impl(const uint16_t* x, const float* Wr, const float* br,
                           const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
@@ -303,7 +313,15 @@ moe_status_t forward_impl(const uint16_t* x, const float* Wr, const float* br,
     return MOE_ERROR_MISALIGNED;
   MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
   MOE_TRY(check_device());
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return forward_launch(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, E, k,
+                        out, ws, static_cast<hipStream_t>(stream), mx6, nullptr);
+}
+
+moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
+                            const uint8_t* w13_codes, const uint8_t* w13_scales,
+                            const uint16_t* b13, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                            const uint16_t* b2, int T, int E, int k, float* out, void* ws,
+                            hipStream_t s, bool mx6, const uint16_t* resid) {
   const WsLayout l = layout(T, E, k);
   char* base = static_cast<char*>(ws);
   int32_t* ids = reinterpret_cast<int32_t*>(base + l.ids);
@@ -316,10 +334,12 @@ moe_status_t forward_impl(const uint16_t* x, const float* Wr, const float* br,
   const int n = T * k;
   // router + top-k + softmax + expert permutation
   const bool tiles = moe::ffn_uses_tiles(n, E);
-  // The weight-streaming schedule needs no permutation arrays: its waves
-  // find their slots in the routing ids.
-  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, tiles ? nullptr : out,
-                                         scratch, tiles ? counts : nullptr, offsets, sorted, s), s));
+  // The weight-streaming schedule needs no permutation arrays (its waves
+  // find their slots in the routing ids) and accumulates into out, which the
+  // router initialises (to the residual, if any).
+  const moe::OutInit init{tiles ? nullptr : out, resid};
+  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, init, scratch,
+                                         tiles ? counts : nullptr, offsets, sorted, s), s));
   FfnArgs a13 = ffn_args(x, offsets, sorted, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
   a13.h_out = h;
   if (!tiles) {
@@ -333,18 +353,18 @@ moe_status_t forward_impl(const uint16_t* x, const float* Wr, const float* br,
   MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));
   FfnArgs a2 = ffn_args(h, offsets, sorted, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
   if (!tiles) {
-    // few rows per expert: the down projection adds w * y into the cleared out
+    // few rows per expert: the down projection adds w * y into out
     a2.ids = ids;
     a2.n_slots = n;
     a2.topk_w = w;
     a2.out = out;
     return after_launch(moe::launch_ffn(a2, moe::EPI_COMBINE, n, s), s);
   }
-  // many rows: store y per slot, then out[t] = sum_j w[t, j] y[t*k + j]
+  // many rows: store y per slot, then out[t] = resid[t] + sum_j w[t, j] y[t*k + j]
   float* y = reinterpret_cast<float*>(base + l.y);
   a2.y_out = y;
   MOE_TRY(after_launch(moe::launch_ffn(a2, moe::EPI_STORE_Y, n, s), s));
-  return after_launch(moe::launch_combine(y, w, T, k, out, s), s);
+  return after_launch(moe::launch_combine(y, w, T, k, resid, out, s), s);
 }
 
 }  // namespace
@@ -366,6 +386,39 @@ moe_status_t moe_forward_mx6(const uint16_t* x, const float* Wr, const float* br
                              float* out, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, E, k, out,
                       ws, ws_bytes, stream, true);
+}
+
+moe_status_t moe_rmsnorm(const uint16_t* x, const float* scale, float eps, int T, uint16_t* t,
+                         void* stream) {
+  if (T < 0 || T > MOE_MAX_ROUTED || !(eps >= 0.f) || !(eps < 1e30f)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !scale || !t) return MOE_ERROR_INVALID_VALUE;
+  if (!aligned(x, 16) || !aligned(t, 16) || !aligned(scale, 16)) return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(moe::launch_rmsnorm(x, scale, eps, T, t, s), s);
+}
+
+moe_status_t moe_forward_block(const uint16_t* x, const float* norm_scale, float norm_eps,
+                               const float* Wr, const float* br, const uint8_t* w13_codes,
+                               const uint8_t* w13_scales, const uint16_t* b13,
+                               const uint8_t* w2_codes, const uint8_t* w2_scales,
+                               const uint16_t* b2, int T, int E, int k, float* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!sizes_ok(T, E, k) || !(norm_eps >= 0.f) || !(norm_eps < 1e30f)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !norm_scale || !Wr || !br || !out) return MOE_ERROR_INVALID_VALUE;
+  MOE_TRY(check_weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2));
+  if (!aligned(x, 16) || !aligned(norm_scale, 16) || !aligned(Wr, 16) || !aligned(out, 16) ||
+      !aligned(br, 4))
+    return MOE_ERROR_MISALIGNED;
+  MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
+  MOE_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* t = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + layout(T, E, k).xnorm);
+  MOE_TRY(after_launch(moe::launch_rmsnorm(x, norm_scale, norm_eps, T, t, s), s));
+  return forward_launch(t, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, E, k, out,
+                        ws, s, false, x);
 }
 
 moe_status_t moe_encode_mx6(const uint16_t* x, int rows, uint8_t* records, void* stream) {

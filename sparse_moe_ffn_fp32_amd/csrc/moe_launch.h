@@ -38,11 +38,19 @@ struct FfnArgs {
   const uint8_t* act6;
 };
 
-// Router + top-k + softmax. `zero_out` (optional) is cleared for the
-// accumulating down projection; with `counts` non-null the expert permutation
-// is built as well. `scratch` holds route_scratch_bytes(T, E) bytes.
+// The layer output before an accumulating down projection: when `out` is
+// set the router kernels write out = float(resid) (a bf16 [T, 2880]
+// residual), or zeros when resid is null.
+struct OutInit {
+  float* out;
+  const uint16_t* resid;
+};
+
+// Router + top-k + softmax, plus the optional output initialisation; with
+// `counts` non-null the expert permutation is built as well. `scratch` holds
+// route_scratch_bytes(T, E) bytes.
 hipError_t launch_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
-                        int32_t* ids, float* w, float* logits, float* zero_out, float* scratch,
+                        int32_t* ids, float* w, float* logits, OutInit init, float* scratch,
                         int32_t* counts, int32_t* offsets, int32_t* sorted_rows, hipStream_t s);
 size_t route_scratch_bytes(int T, int E);
 
@@ -70,6 +78,12 @@ bool ffn_uses_tiles(int n_rows, int E);
 // bf16 rows [rows, 2880] -> two-piece MX FP6 records [rows, 23, 256 B]
 hipError_t launch_mx6_encode(const uint16_t* x, int rows, uint8_t* rec, hipStream_t s);
 
-hipError_t launch_combine(const float* y, const float* w, int T, int k, float* out, hipStream_t s);
+// out[t] = resid[t] (bf16, optional) + sum_j w[t, j] y[t*k + j]
+hipError_t launch_combine(const float* y, const float* w, int T, int k, const uint16_t* resid,
+                          float* out, hipStream_t s);
+
+// t = bf16(x / sqrt(mean(x^2) + eps) * scale) per row of x [T, 2880] bf16
+hipError_t launch_rmsnorm(const uint16_t* x, const float* scale, float eps, int T, uint16_t* t,
+                          hipStream_t s);
 
 }  // namespace moe

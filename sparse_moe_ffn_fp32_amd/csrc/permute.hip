@@ -171,6 +171,7 @@ hipError_t launch_permute(const int32_t* ids, int n, int E, int k, int32_t* coun
 // experts' outputs; one thread per 4 output elements).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const float* __restrict__ w, int T, int k,
+                                                      const uint16_t* __restrict__ resid,
                                                       float* __restrict__ out) {
   constexpr int C4 = kH / 4;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -178,6 +179,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = (int)(idx / C4);
   const int c = (int)(idx % C4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (resid) {
+    const uint2 r = reinterpret_cast<const uint2*>(resid)[idx];
+    acc = make_float4(bf16_bits_to_f32(r.x & 0xFFFFu), bf16_bits_to_f32(r.x >> 16),
+                      bf16_bits_to_f32(r.y & 0xFFFFu), bf16_bits_to_f32(r.y >> 16));
+  }
   for (int j = 0; j < k; ++j) {
     const float wt = w[(size_t)t * k + j];
     const float4 v = reinterpret_cast<const float4*>(y)[((size_t)t * k + j) * C4 + c];
@@ -189,10 +195,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   reinterpret_cast<float4*>(out)[(size_t)t * C4 + c] = acc;
 }
 
-hipError_t launch_combine(const float* y, const float* w, int T, int k, float* out, hipStream_t s) {
+hipError_t launch_combine(const float* y, const float* w, int T, int k, const uint16_t* resid,
+                          float* out, hipStream_t s) {
   const long long n4 = (long long)T * (kH / 4);
   const unsigned blocks = (unsigned)((n4 + 255) / 256);
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, y, w, T, k, out);
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, y, w, T, k, resid, out);
   return hipGetLastError();
 }
 

@@ -205,3 +205,32 @@ def test_gate_up_mx6_validation(L):
     assert g(xr=A + 8) == MISALIGNED
     assert g(s=A + 2) == MISALIGNED
     assert g(b=A + 4) == MISALIGNED
+
+
+def test_forward_block_validation(L):
+    def f(T=4, E=32, k=4, x=A, g=A, eps=1e-5, out=A, ws=A, nbytes=None):
+        if nbytes is None:
+            nbytes = L.moe_workspace_size(max(T, 0), E, k)
+        return L.moe_forward_block(P(x), P(g), eps, P(A), P(A), P(A), P(A), P(A), P(A), P(A), P(A),
+                                   T, E, k, P(out), P(ws), nbytes, None)
+    assert f(T=0) == OK
+    assert f(T=-1) == INVALID
+    assert f(eps=-1.0) == INVALID
+    assert f(eps=float("nan")) == INVALID
+    assert f(g=None) == INVALID
+    assert f(x=None) == INVALID
+    assert f(g=A + 8) == MISALIGNED
+    assert f(out=A + 4) == MISALIGNED
+    assert f(ws=None) == WORKSPACE
+    assert f(nbytes=L.moe_workspace_size(4, 32, 4) - 1) == WORKSPACE
+
+
+def test_rmsnorm_validation(L):
+    n = lambda T=4, x=A, g=A, eps=1e-5, t=A: L.moe_rmsnorm(P(x), P(g), eps, T, P(t), None)
+    assert n(T=0) == OK
+    assert n(T=-1) == INVALID
+    assert n(eps=-0.5) == INVALID
+    assert n(x=None) == INVALID
+    assert n(t=None) == INVALID
+    assert n(g=A + 4) == MISALIGNED
+    assert n(t=A + 2) == MISALIGNED
