@@ -261,7 +261,7 @@ def main() -> int:
         achieved = alg / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP6_FP4_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP6_FP4_PEAK_TFLOPS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(workload + " mx6"),
                 "kernel": "ffn_wide6_kernel<EPI_SWIGLU> (gate/up + SwiGLU, FP4 x FP6 pieces)",
                 "algorithmic_flop_per_launch": alg,
                 "mfma_flop_issued_per_launch": 2 * alg,
