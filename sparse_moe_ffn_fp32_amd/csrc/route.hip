@@ -449,6 +449,54 @@ __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(
   }
 }
 
+// The same sums, top-k and softmax as route_finish_kernel without the
+// permutation, spread over blocks of 256 / E tokens each (one thread per
+// (token, expert) pair), so that the partial-logit loads of a decode batch
+// run on many CUs instead of one. Arithmetic in the same order: identical
+// expert choices and weights.
+__global__ __launch_bounds__(256) void route_finish_tiles_kernel(
+    const float* __restrict__ partial, const float* __restrict__ br, int T, int E, int k, int tb,
+    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits) {
+  __shared__ float lg[256];
+  __shared__ float sel_v[256];
+  __shared__ int sel_e[256];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * tb;
+  const int nt = min(tb, T - t0);
+  const int TE = T * E;
+  const int np = nt * E;
+  float v = 0.f;
+  if (tid < np) {
+    const int i = t0 * E + tid;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < kRouteChunks; ++c) acc += partial[(size_t)c * TE + i];
+    v = acc + br[tid % E];
+    lg[tid] = v;
+    if (logits) logits[i] = v;
+  }
+  __syncthreads();
+  if (tid < np) {
+    const int tl = tid / E, e = tid - tl * E;
+    const float* row = lg + tl * E;
+    int rank = 0;
+    for (int e2 = 0; e2 < E; ++e2) rank += better(row[e2], e2, v, e) ? 1 : 0;
+    if (rank < k) {
+      sel_v[tl * k + rank] = v;
+      sel_e[tl * k + rank] = e;
+    }
+  }
+  __syncthreads();
+  if (tid < nt * k) {
+    const int tl = tid / k;
+    const float m = sel_v[tl * k];
+    float z = 0.f;
+    for (int j = 0; j < k; ++j) z += __expf(sel_v[tl * k + j] - m);
+    ids[t0 * k + tid] = sel_e[tid];
+    wts[t0 * k + tid] = __expf(sel_v[tid] - m) / z;
+  }
+}
+
 template <bool PERMUTE>
 static void launch_finish(const float* scratch, const float* br, int T, int E, int k, int32_t* ids,
                           float* w, float* logits, int32_t* counts, int32_t* offsets,
@@ -472,10 +520,13 @@ static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const floa
   if (few_tokens(T, E)) {
     const dim3 grid((T + 31) / 32, kRouteChunks);
     hipLaunchKernelGGL((route_partial_kernel<MT>), grid, dim3(64), 0, s, x, Wr, T, E, scratch, init);
-    if (counts)
+    if (counts) {
       launch_finish<true>(scratch, br, T, E, k, ids, w, logits, counts, offsets, sorted_rows, s);
-    else
-      launch_finish<false>(scratch, br, T, E, k, ids, w, logits, counts, offsets, sorted_rows, s);
+    } else {
+      const int tb = 256 / E;   // tokens per block; E <= 256
+      hipLaunchKernelGGL(route_finish_tiles_kernel, dim3((T + tb - 1) / tb), dim3(256), 0, s, scratch,
+                         br, T, E, k, tb, ids, w, logits);
+    }
     return hipGetLastError();
   }
   const int blocks = (T + 31) / 32;
