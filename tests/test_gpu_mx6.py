@@ -167,3 +167,39 @@ def test_forward_mx6_config_sampled(idx):
     ref = oracle.forward(inp, c.k, tokens=sample, ids_override=ids_h)
     m = assert_out_close(np_(out)[sample], ref["out"], c.name)
     say(f"  sampled metrics {m}; mx6 vs bf16 path, all rows {m_all}")
+
+
+@pytest.mark.parametrize("T,E,k", [(16, 32, 4), (300, 4, 1)])
+def test_gate_up_mx6(T, E, k):
+    """The standalone gate/up entry point on encoded activations (always the
+    tiled kernel, also for few rows) against the exact h of the oracle's
+    definition, row for row in expert-sorted order."""
+    say(f"gate_up_mx6 T={T} E={E} k={k}")
+    inp = make_layer_inputs(T, E, k, seed=8000 + T + E)
+    d = to_device(inp)
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+    counts, offsets, rows = moe.permute(ids, E)
+    p13c, p13s, b13, _, _, _ = weights_args(d)
+    xrec = moe.encode_mx6(d["x"])
+    h = moe.gate_up_mx6(xrec, offsets, rows, p13c, p13s, b13, k=k)
+    h_bf16 = moe.gate_up(d["x"], offsets, rows, p13c, p13s, b13, k=k)
+    torch.cuda.synchronize()
+    x64 = oracle.bf16_to_f64(inp["x"])
+    h_got = oracle.bf16_to_f64(np_(h).view(np.uint16))
+    off, srt = np_(offsets), np_(rows)
+    ref = np.zeros_like(h_got)
+    for e in range(E):
+        if off[e + 1] == off[e]:
+            continue
+        W13, b13e, _, _ = oracle.expert_weights(inp, e)
+        toks = srt[off[e]:off[e + 1]] // k
+        ref[off[e]:off[e + 1]] = oracle.swiglu(x64[toks] @ W13.T + b13e)
+    # h is an intermediate with a heavy tail (the bar of the layer output is
+    # applied to the output): both paths are held to the mean per-row
+    # relative L2 of the layer bar, and the pieces may not more than double
+    # the largest error of the bf16 path's h (rounded to bf16 itself)
+    m6 = out_metrics(h_got, ref)
+    mb = out_metrics(oracle.bf16_to_f64(np_(h_bf16).view(np.uint16)), ref)
+    say(f"  h metrics: pieces {m6}; bf16 path {mb}")
+    assert m6["finite"] and m6["mean_rel_l2"] <= 5e-3 and mb["mean_rel_l2"] <= 5e-3
+    assert m6["max_err_over_rms"] <= 2 * mb["max_err_over_rms"], (m6, mb)
