@@ -107,6 +107,9 @@ def main() -> int:
                     help="tiled expert GEMMs on bf16 activations (moe_forward) or on two-piece "
                          "MX FP6 activations with the block-scaled FP4 matrix cores "
                          "(moe_forward_mx6)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each step (one per weight copy) into a HIP graph once and time "
+                         "the replays")
     ap.add_argument("--block", action="store_true",
                     help="time the decoder sublayer x + layer(RMSNorm(x)) (moe_forward_block) "
                          "instead of the layer alone")
@@ -173,6 +176,28 @@ def main() -> int:
             return
         fwd(x, w["Wr"], w["br"], w["w13_codes"], w["w13_scales"], w["b13"],
             w["w2_codes"], w["w2_scales"], w["b2"], k=k, out=out, workspace=ws)
+
+    if args.graph:
+        eager_step = step
+        for i in range(copies):
+            eager_step(i)
+        torch.cuda.synchronize()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for i in range(copies):
+                eager_step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(copies):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                eager_step(i)
+            graphs.append(gph)
+
+        def step(i):
+            graphs[i % copies].replay()
 
     for i in range(args.warmup):
         step(i)
@@ -295,7 +320,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": workload, "T": T, "E": E, "k": k, "hidden": H,
                    "intermediate": I, "weights": "MXFP4 (E2M1 + E8M0 per 32)",
-                   "weight_copies_rotated": copies, "seed": args.seed},
+                   "weight_copies_rotated": copies, "seed": args.seed,
+                   "hip_graph": bool(args.graph)},
         "roofline": roof,
         "layer_roofline_frac": round(layer_frac, 4),
         "experts_touched": touched,
