@@ -14,10 +14,10 @@
 //
 // Two schedules, chosen by T (both deterministic, fixed summation order):
 //  * few tokens (T <= 128, T*E <= 4096): the K dimension is cut into 20 chunks, one wave
-//    per (32-token tile, chunk) writes partial logits to scratch; a single
-//    1024-thread block adds the 20 partials in chunk order, adds the bias,
-//    selects the top k and, when asked, also builds the expert permutation
-//    (two small launches for all routing).
+//    per (32-token tile, chunk) writes partial logits to scratch; a second
+//    launch adds the 20 partials in chunk order, adds the bias and selects
+//    the top k: blocks of 256/E tokens when no permutation is wanted, or a
+//    single 1024-thread block that also builds the expert permutation.
 //  * many tokens: a block per 32 tokens, its waves split K and add their
 //    partial tiles in wave order through LDS, then select the top k and
 //    count the block's routed slots per expert for the parallel permutation.
