@@ -30,7 +30,10 @@
 //  * tiled ("wide", many rows per expert: prefill). A 256-thread block owns
 //    four 64-row groups x 64 tokens; the gathered activation tile goes
 //    through a double-buffered LDS ring (128 K per step), weights straight to
-//    registers as above; blocks are numbered XCD by XCD.
+//    registers as above; blocks are numbered XCD by XCD. Its block-scaled
+//    variant (ffn_wide6_kernel) reads the activations as two-piece MX FP6
+//    records instead and feeds them, with the packed FP4 weights unconverted,
+//    to the FP4 x FP6 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4).
 #include "moe_device.h"
 #include "moe_launch.h"
 
