@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     LAYER_CONFIGS,
     LayerConfig,
     bf16_bits_from_f32,
+    device_activations,
     make_layer_inputs,
     make_config_inputs,
     zipf_target_shares,

@@ -165,3 +165,21 @@ def make_layer_inputs(T: int, E: int, k: int, seed: int = 0,
 def make_config_inputs(index: int, seed: int = 0, router_only: bool = False) -> Dict[str, np.ndarray]:
     c = LAYER_CONFIGS[index]
     return make_layer_inputs(c.T, c.E, c.k, seed=seed, zipf_s=c.zipf_s, router_only=router_only)
+
+
+def device_activations(T: int, seed: int = 0, H: int = H_DEFAULT, device="cuda"):
+    """x [T, H] as bf16 bit patterns (int16 tensor) drawn on the device: float32
+    N(0, 1) from torch's generator for that device seeded with ``seed``,
+    rounded to bf16 (nearest even). The distribution of ``make_layer_inputs``'
+    x, for row counts whose host draw would take minutes; the values differ
+    from the host draw. Read rows back to the host for the oracle."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    chunk = 1 << 16
+    for r0 in range(0, T, chunk):
+        n = min(chunk, T - r0)
+        x[r0:r0 + n] = torch.randn((n, H), generator=g, device=device,
+                                   dtype=torch.float32).to(torch.bfloat16)
+    return x.view(torch.int16)

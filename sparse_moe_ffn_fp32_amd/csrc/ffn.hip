@@ -372,7 +372,7 @@ struct X6Half {
   }
 };
 
-// s_waitcnt with only a vmcnt limit// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
+// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
