@@ -197,7 +197,7 @@ __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, con
     const int re = min(e_end, rb + kSkBT);
     const int p = rb + r;
     const bool tok_ok = p < re;
-    // padded token columns read the tile's first row: their outputs are dropped
+    // padded token columns take the tile's first slot; their outputs are dropped
     int slot;
     if (a.ids) {
       int sr = slot_first;
@@ -232,10 +232,15 @@ __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, con
         for (int mt = 0; mt < 4; ++mt) st.w[4 * q + mt] = w4[mt];
       }
     };
+    // With one group per wave (the down projection) only the lanes of real
+    // token columns load: a decode tile is often half empty. Measured on the
+    // two-group wave (gate/up) the branch costs more than the loads it saves.
     auto issue_x = [&](SkStage<RG>& st, int s) __attribute__((always_inline)) {
       const int kb = min(4 * s + g, kKB - 1);
+      if (RG > 1 || tok_ok) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.xv[i] = *reinterpret_cast<const uint4*>(xp + kb * 32 + 8 * i);
+        for (int i = 0; i < 4; ++i) st.xv[i] = *reinterpret_cast<const uint4*>(xp + kb * 32 + 8 * i);
+      }
     };
 
     f32x4 acc[MT];
@@ -260,6 +265,12 @@ __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, con
     // fully unrolled K loop with a kSkDepth-step register prefetch ring
     // (the first weight stages go out before the activations may be read)
     SkStage<RG> st[kSkDepth];
+    if constexpr (RG == 1) {
+#pragma unroll
+      for (int q = 0; q < kSkDepth; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[q].xv[i] = make_uint4(0u, 0u, 0u, 0u);   // empty token columns
+    }
 #pragma unroll
     for (int q = 0; q < kSkDepth; ++q) issue_w(st[q], q);
     if (rb == e_begin) wait_act();

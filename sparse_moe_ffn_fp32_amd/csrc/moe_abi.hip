@@ -40,11 +40,10 @@ WsLayout layout(int T, int E, int k) {
   l.sorted = off;   off = align_up(off + n * 4);
   l.scratch = off;  off = align_up(off + moe::route_scratch_bytes(T, E));
   l.h = off;        off = align_up(off + n * (size_t)moe::kI * 2);
-  // per-slot fp32 expert outputs: the many-rows schedule stores them and sums
-  // a token's k rows in a second pass instead of atomically adding into out
-  l.y = off;
+  // per-slot fp32 expert outputs: the layer stores them and sums a token's k
+  // rows in a second pass instead of atomically adding into out
+  l.y = off;        off = align_up(off + n * (size_t)moe::kH * 4);
   const bool tiles = n > 0 && moe::ffn_uses_tiles((int)n, E);
-  if (tiles) off = align_up(off + n * (size_t)moe::kH * 4);
   // the tiled schedule of moe_forward_mx6: x as two-piece MX FP6 records
   l.xrec = off;
   if (tiles) off = align_up(off + (size_t)T * moe::kRowRecBytes);
@@ -334,11 +333,10 @@ moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
   const int n = T * k;
   // router + top-k + softmax + expert permutation
   const bool tiles = moe::ffn_uses_tiles(n, E);
-  // The weight-streaming schedule needs no permutation arrays (its waves
-  // find their slots in the routing ids) and accumulates into out, which the
-  // router initialises (to the residual, if any).
-  const moe::OutInit init{tiles ? nullptr : out, resid};
-  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, init, scratch,
+  // The weight-streaming schedule needs no permutation arrays: its waves find
+  // their slots in the routing ids.
+  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr,
+                                         moe::OutInit{nullptr, nullptr}, scratch,
                                          tiles ? counts : nullptr, offsets, sorted, s), s));
   FfnArgs a13 = ffn_args(x, offsets, sorted, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
   a13.h_out = h;
@@ -353,14 +351,13 @@ moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
   MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));
   FfnArgs a2 = ffn_args(h, offsets, sorted, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
   if (!tiles) {
-    // few rows per expert: the down projection adds w * y into out
     a2.ids = ids;
     a2.n_slots = n;
-    a2.topk_w = w;
-    a2.out = out;
-    return after_launch(moe::launch_ffn(a2, moe::EPI_COMBINE, n, s), s);
   }
-  // many rows: store y per slot, then out[t] = resid[t] + sum_j w[t, j] y[t*k + j]
+  // Store y per slot, then out[t] = resid[t] + sum_j w[t, j] y[t*k + j] in a
+  // fixed order. Adding w * y into out atomically from the down epilogue
+  // instead costs more than the extra pass: the T*k*2880 fp32 atomics are
+  // served far from the CUs at a fraction of the store rate.
   float* y = reinterpret_cast<float*>(base + l.y);
   a2.y_out = y;
   MOE_TRY(after_launch(moe::launch_ffn(a2, moe::EPI_STORE_Y, n, s), s));

@@ -23,12 +23,13 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
-# (T, E, k, fn): the weight-streaming schedule (atomic down epilogue: the
-# order of a token's k additions may differ, so the bar is a relative 1e-6),
-# and the tiled one (fixed-order combine: bit for bit)
-@pytest.mark.parametrize("T,E,k,path,exact", [(64, 32, 4, "bf16", False), (256, 8, 4, "bf16", True),
-                                              (256, 8, 4, "mx6", True), (16, 32, 4, "block", False)])
-def test_forward_graph_replays(T, E, k, path, exact):
+# (T, E, k, path): the weight-streaming schedule (T=64, E=32; T=16 with the
+# norm and residual) and the tiled one, bf16 and FP6 pieces. Both schedules
+# sum a token's k expert outputs in a fixed order, so every replay must
+# reproduce the eager output bit for bit.
+@pytest.mark.parametrize("T,E,k,path", [(64, 32, 4, "bf16"), (256, 8, 4, "bf16"),
+                                        (256, 8, 4, "mx6"), (16, 32, 4, "block")])
+def test_forward_graph_replays(T, E, k, path):
     print(f"graph T={T} E={E} k={k} {path}", flush=True)
     inp = make_layer_inputs(T, E, k, seed=9000 + T + E)
     d = to_device(inp)
@@ -57,7 +58,6 @@ def test_forward_graph_replays(T, E, k, path, exact):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
-    scale = float(eager.abs().max())
     for r in range(3):
         out.fill_(float("nan"))            # eager work between replays
         ws.fill_(0xCD)
@@ -66,8 +66,4 @@ def test_forward_graph_replays(T, E, k, path, exact):
         torch.cuda.synchronize()
         got = out.clone()
         assert torch.isfinite(got).all(), f"replay {r}: non-finite"
-        if exact:
-            assert torch.equal(got, eager), f"replay {r} differs"
-        else:
-            err = float((got - eager).abs().max())
-            assert err <= 1e-6 * scale, (r, err, scale)
+        assert torch.equal(got, eager), f"replay {r} differs"

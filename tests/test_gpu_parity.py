@@ -270,7 +270,12 @@ def test_forward_config_full_oracle(idx):
     d = to_device(inp)
     ids, w = moe.route(d["x"], d["Wr"], d["br"], k=c.k)
     out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=c.k)
+    # the same kernels through the separate calls: identical bits (per-slot
+    # outputs, then a fixed-order weighted sum)
+    counts, offsets, rows = moe.permute(ids, c.E)
+    out_calls = moe.combine(moe.expert_ffn(d["x"], offsets, rows, *weights_args(d), k=c.k), w)
     torch.cuda.synchronize()
+    assert torch.equal(out, out_calls)
     ref = oracle.forward(inp, c.k, ids_override=np_(ids))
     n_tie = check_routing(np_(ids), np_(w), ref["logits"], c.k)
     m = assert_out_close(np_(out), ref["out"], c.name)
@@ -292,7 +297,7 @@ def test_forward_config_sampled(idx):
     ids_h = np_(ids)
     logits = oracle.router_logits(inp["x"], inp["Wr"], inp["br"])
     n_tie = check_routing(ids_h, np_(w), logits, c.k)
-    # every row: fused epilogue (atomic weighted sum) vs unfused y + combine
+    # every row: the one-call layer vs the separate calls (expert_ffn + combine)
     m_all = out_metrics(np_(out), np_(out_unfused).astype(np.float64))
     assert m_all["max_err_over_rms"] < 1e-4, m_all
     # sampled rows against the oracle (first, last and random tokens)
