@@ -162,8 +162,8 @@ moe_status_t moe_route(const uint16_t* x, const float* Wr, const float* br, int 
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* scratch = reinterpret_cast<float*>(static_cast<char*>(ws) + layout(T, E, k).scratch);
-  return after_launch(moe::launch_route(x, Wr, br, T, E, k, topk_ids, topk_w, logits, moe::OutInit{nullptr, nullptr},
-                                        scratch, nullptr, nullptr, nullptr, s), s);
+  return after_launch(moe::launch_route(x, Wr, br, T, E, k, topk_ids, topk_w, logits, scratch, nullptr,
+                                        nullptr, nullptr, s), s);
 }
 
 moe_status_t moe_pack_weights(const uint8_t* codes, const uint8_t* scales, int E, int N,
@@ -335,8 +335,7 @@ moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
   const bool tiles = moe::ffn_uses_tiles(n, E);
   // The weight-streaming schedule needs no permutation arrays: its waves find
   // their slots in the routing ids.
-  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr,
-                                         moe::OutInit{nullptr, nullptr}, scratch,
+  MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, scratch,
                                          tiles ? counts : nullptr, offsets, sorted, s), s));
   FfnArgs a13 = ffn_args(x, offsets, sorted, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
   a13.h_out = h;

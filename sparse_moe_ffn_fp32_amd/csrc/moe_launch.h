@@ -38,19 +38,10 @@ struct FfnArgs {
   const uint8_t* act6;
 };
 
-// The layer output before an accumulating down projection: when `out` is
-// set the router kernels write out = float(resid) (a bf16 [T, 2880]
-// residual), or zeros when resid is null.
-struct OutInit {
-  float* out;
-  const uint16_t* resid;
-};
-
-// Router + top-k + softmax, plus the optional output initialisation; with
-// `counts` non-null the expert permutation is built as well. `scratch` holds
-// route_scratch_bytes(T, E) bytes.
+// Router + top-k + softmax; with `counts` non-null the expert permutation is
+// built as well. `scratch` holds route_scratch_bytes(T, E) bytes.
 hipError_t launch_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
-                        int32_t* ids, float* w, float* logits, OutInit init, float* scratch,
+                        int32_t* ids, float* w, float* logits, float* scratch,
                         int32_t* counts, int32_t* offsets, int32_t* sorted_rows, hipStream_t s);
 size_t route_scratch_bytes(int T, int E);
 

@@ -245,27 +245,6 @@ __device__ __forceinline__ void lanes_topk(const float* lg, int e_stride, int E,
 
 constexpr int kTopkLanes = 8;   // lanes per token in the top-k
 
-// Slice `part` of `parts` of the layer output before the accumulating down
-// projection: out = float(resid) when a residual is given, else 0.
-__device__ __forceinline__ void init_rows_slice(const OutInit& init, int T, int part, int parts,
-                                                int tid, int nthreads) {
-  const long long total4 = (long long)T * (kH / 4);
-  const long long per = (total4 + parts - 1) / parts;
-  const long long b = (long long)part * per;
-  const long long end = min(total4, b + per);
-  float4* o = reinterpret_cast<float4*>(init.out);
-  if (init.resid) {
-    const uint2* r = reinterpret_cast<const uint2*>(init.resid);
-    for (long long i = b + tid; i < end; i += nthreads) {
-      const uint2 v = r[i];
-      o[i] = make_float4(bf16_bits_to_f32(v.x & 0xFFFFu), bf16_bits_to_f32(v.x >> 16),
-                         bf16_bits_to_f32(v.y & 0xFFFFu), bf16_bits_to_f32(v.y >> 16));
-    }
-  } else {
-    for (long long i = b + tid; i < end; i += nthreads) o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-}
-
 // ---------------------------------------------------------------- many tokens
 template <int MT, int WK>
 __global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restrict__ x,
@@ -274,7 +253,6 @@ __global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restri
                                                         int k, int32_t* __restrict__ ids,
                                                         float* __restrict__ wts,
                                                         float* __restrict__ logits,
-                                                        OutInit init,
                                                         int32_t* __restrict__ block_hist) {
   constexpr int KW = kH / WK;      // K range of one wave
   constexpr int KSTEPS = KW / 16;  // MFMA steps of one wave
@@ -327,7 +305,6 @@ __global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restri
     lanes_topk<kTopkLanes>(red + tt, LDR, E, k, t < T, ids + (size_t)t * k, wts + (size_t)t * k,
                            nullptr);
   }
-  if (init.out) init_rows_slice(init, T, blockIdx.x, gridDim.x, threadIdx.x, WK * 64);
   if (block_hist) {
     // expert histogram of this block's routed slots, for the parallel permutation
     int* hist = reinterpret_cast<int*>(red);   // the logits tile is no longer needed
@@ -345,8 +322,7 @@ __global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restri
 template <int MT>
 __global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ Wr, int T,
-                                                           int E, float* __restrict__ partial,
-                                                           OutInit init) {
+                                                           int E, float* __restrict__ partial) {
   const int lane = threadIdx.x;
   const int n = lane & 31;
   const int hh = lane >> 5;
@@ -370,8 +346,6 @@ __global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __res
           if (e < E) prow[e] = acc[mt][4 * q + j];
         }
   }
-  if (init.out)
-    init_rows_slice(init, T, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y, lane, 64);
 }
 
 // One 1024-thread block: logits = bias + sum of the chunk partials in chunk
@@ -514,12 +488,12 @@ static void launch_finish(const float* scratch, const float* br, int T, int E, i
 // ---------------------------------------------------------------- launch
 template <int MT>
 static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const float* br, int T, int E,
-                                  int k, int32_t* ids, float* w, float* logits, OutInit init,
+                                  int k, int32_t* ids, float* w, float* logits,
                                   float* scratch, int32_t* counts, int32_t* offsets,
                                   int32_t* sorted_rows, hipStream_t s) {
   if (few_tokens(T, E)) {
     const dim3 grid((T + 31) / 32, kRouteChunks);
-    hipLaunchKernelGGL((route_partial_kernel<MT>), grid, dim3(64), 0, s, x, Wr, T, E, scratch, init);
+    hipLaunchKernelGGL((route_partial_kernel<MT>), grid, dim3(64), 0, s, x, Wr, T, E, scratch);
     if (counts) {
       launch_finish<true>(scratch, br, T, E, k, ids, w, logits, counts, offsets, sorted_rows, s);
     } else {
@@ -538,14 +512,14 @@ static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const floa
   if constexpr (MT == 1) {
     if (blocks < 256) {
       hipLaunchKernelGGL((route_kernel<1, 12>), dim3(blocks), dim3(12 * 64), lds, s, x, Wr, br, T, E,
-                         k, ids, w, logits, init, counts ? hist : nullptr);
+                         k, ids, w, logits, counts ? hist : nullptr);
     } else {
       hipLaunchKernelGGL((route_kernel<1, 4>), dim3(blocks), dim3(4 * 64), lds, s, x, Wr, br, T, E,
-                         k, ids, w, logits, init, counts ? hist : nullptr);
+                         k, ids, w, logits, counts ? hist : nullptr);
     }
   } else {
     hipLaunchKernelGGL((route_kernel<MT, 4>), dim3(blocks), dim3(4 * 64), lds, s, x, Wr, br, T, E, k,
-                       ids, w, logits, init, counts ? hist : nullptr);
+                       ids, w, logits, counts ? hist : nullptr);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !counts) return err;
@@ -553,17 +527,17 @@ static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const floa
 }
 
 hipError_t launch_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
-                        int32_t* ids, float* w, float* logits, OutInit init, float* scratch,
+                        int32_t* ids, float* w, float* logits, float* scratch,
                         int32_t* counts, int32_t* offsets, int32_t* sorted_rows, hipStream_t s) {
   switch ((E + 31) / 32) {
-    case 1: return launch_route_mt<1>(x, Wr, br, T, E, k, ids, w, logits, init, scratch, counts, offsets, sorted_rows, s);
-    case 2: return launch_route_mt<2>(x, Wr, br, T, E, k, ids, w, logits, init, scratch, counts, offsets, sorted_rows, s);
-    case 3: return launch_route_mt<3>(x, Wr, br, T, E, k, ids, w, logits, init, scratch, counts, offsets, sorted_rows, s);
-    case 4: return launch_route_mt<4>(x, Wr, br, T, E, k, ids, w, logits, init, scratch, counts, offsets, sorted_rows, s);
-    case 5: return launch_route_mt<5>(x, Wr, br, T, E, k, ids, w, logits, init, scratch, counts, offsets, sorted_rows, s);
-    case 6: return launch_route_mt<6>(x, Wr, br, T, E, k, ids, w, logits, init, scratch, counts, offsets, sorted_rows, s);
-    case 7: return launch_route_mt<7>(x, Wr, br, T, E, k, ids, w, logits, init, scratch, counts, offsets, sorted_rows, s);
-    case 8: return launch_route_mt<8>(x, Wr, br, T, E, k, ids, w, logits, init, scratch, counts, offsets, sorted_rows, s);
+    case 1: return launch_route_mt<1>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
+    case 2: return launch_route_mt<2>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
+    case 3: return launch_route_mt<3>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
+    case 4: return launch_route_mt<4>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
+    case 5: return launch_route_mt<5>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
+    case 6: return launch_route_mt<6>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
+    case 7: return launch_route_mt<7>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
+    case 8: return launch_route_mt<8>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
     default: return hipErrorInvalidValue;
   }
 }
