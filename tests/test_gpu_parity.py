@@ -132,6 +132,10 @@ def test_permute(T, E, k):
 # ---------------------------------------------------------------- experts
 # (T, E, k): T*k <= 24*E takes the weight-streaming kernel, above it the tiled one
 SMALL_CASES = [
+    (1, 1, 1),      # one expert: every slot goes to it with weight 1
+    (33, 1, 1),     # the same past the schedule threshold (33 > 24 rows): tiled
+    (48, 8, 4),     # T*k = 24*E exactly: the last weight-streaming shape
+    (49, 8, 4),     # one token more: the first tiled one
     (1, 4, 4),      # every expert selected
     (5, 8, 2),
     (16, 32, 4),    # the 20b T=16 shape
