@@ -350,9 +350,9 @@ __global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __res
 
 // One 1024-thread block: logits = bias + sum of the chunk partials in chunk
 // order (one thread per (token, expert) pair, all partial loads in flight at
-// once), then one wave per token selects the top k from LDS; with PERMUTE the
-// block also builds the expert permutation of the T*k slots.
-template <bool PERMUTE, int PAIRS>
+// once), then the top k of each token by rank, the softmax, and the expert
+// permutation of the T*k slots.
+template <int PAIRS>
 __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(
     const float* __restrict__ partial, const float* __restrict__ br, int T, int E, int k,
     int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits,
@@ -417,10 +417,8 @@ __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(
     ids[i] = lds_ids[i];
     wts[i] = __expf(sel_v[i] - m) / z;
   }
-  if constexpr (PERMUTE) {
-    __syncthreads();
-    block_permute(lds_ids, T * k, E, counts, offsets, sorted_rows, sm);
-  }
+  __syncthreads();
+  block_permute(lds_ids, T * k, E, counts, offsets, sorted_rows, sm);
 }
 
 // The same sums, top-k and softmax as route_finish_kernel without the
@@ -471,13 +469,12 @@ __global__ __launch_bounds__(256) void route_finish_tiles_kernel(
   }
 }
 
-template <bool PERMUTE>
 static void launch_finish(const float* scratch, const float* br, int T, int E, int k, int32_t* ids,
                           float* w, float* logits, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_rows, hipStream_t s) {
   const int pairs = (T * E + kPermThreads - 1) / kPermThreads;
 #define MOE_FINISH(P)                                                                             \
-  hipLaunchKernelGGL((route_finish_kernel<PERMUTE, P>), dim3(1), dim3(kPermThreads), 0, s, scratch, \
+  hipLaunchKernelGGL((route_finish_kernel<P>), dim3(1), dim3(kPermThreads), 0, s, scratch,          \
                      br, T, E, k, ids, w, logits, counts, offsets, sorted_rows)
   if (pairs <= 1) MOE_FINISH(1);
   else if (pairs <= 2) MOE_FINISH(2);
@@ -495,7 +492,7 @@ static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const floa
     const dim3 grid((T + 31) / 32, kRouteChunks);
     hipLaunchKernelGGL((route_partial_kernel<MT>), grid, dim3(64), 0, s, x, Wr, T, E, scratch);
     if (counts) {
-      launch_finish<true>(scratch, br, T, E, k, ids, w, logits, counts, offsets, sorted_rows, s);
+      launch_finish(scratch, br, T, E, k, ids, w, logits, counts, offsets, sorted_rows, s);
     } else {
       const int tb = 256 / E;   // tokens per block; E <= 256
       hipLaunchKernelGGL(route_finish_tiles_kernel, dim3((T + tb - 1) / tb), dim3(256), 0, s, scratch,
