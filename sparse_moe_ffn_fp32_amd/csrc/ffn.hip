@@ -91,14 +91,27 @@ struct GroupStream {
   }
   int lane_c, lane_c_last, lane_s, lane_s_last;
 
-  // four 16-row tiles of step s (s is a compile-time constant after unrolling)
+  // four 16-row tiles of step s (s is a compile-time constant after
+  // unrolling). NT marks the loads non-temporal: a stream read once (the
+  // weight-streaming schedule) then keeps the caches for the activations.
+  template <bool NT = false>
   __device__ __forceinline__ void load(int s, uint4 (&w)[4], uint32_t& sc) const {
     const bool last = s >= kFullSteps;
     const int tstride = last ? 512 : 1024;
     const uint8_t* c = cg + s * kStepCodeBytes + (last ? lane_c_last : lane_c);
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(sg + s * 256 + (last ? lane_s_last : lane_s));
+    if constexpr (NT) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) w[mt] = *reinterpret_cast<const uint4*>(c + mt * tstride);
-    sc = *reinterpret_cast<const uint32_t*>(sg + s * 256 + (last ? lane_s_last : lane_s));
+      for (int mt = 0; mt < 4; ++mt) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c + mt * tstride));
+        w[mt] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+      sc = __builtin_nontemporal_load(sp);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) w[mt] = *reinterpret_cast<const uint4*>(c + mt * tstride);
+      sc = *sp;
+    }
     if (last) {
       const uint32_t keep = half_ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
@@ -227,7 +240,7 @@ __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, con
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         uint4 w4[4];
-        ws[q].load(s, w4, st.sc[q]);
+        ws[q].template load<true>(s, w4, st.sc[q]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) st.w[4 * q + mt] = w4[mt];
       }
