@@ -20,13 +20,14 @@
 // group g, so each MFMA sums over 8 consecutive K of 4 blocks.
 //
 // Two schedules:
-//  * weight-streaming ("skinny", few rows per expert: decode). One wave owns
-//    one or two 64-row groups of one expert and its tokens, 16 at a time;
-//    it streams the groups' code bytes front to back with a 3-step register
-//    prefetch and reads its activations directly (L2-resident).
-//    In the layer's own schedule the wave finds its expert's slots in the
-//    routing ids; through the standalone entry points it reads offsets /
-//    sorted_rows.
+//  * weight-streaming ("skinny", few rows per expert: decode). A workgroup
+//    of three waves owns three 64-row groups of one expert and its tokens,
+//    16 at a time; each wave streams its group's code bytes front to back
+//    (non-temporal loads, 3-step register prefetch), and the workgroup loads
+//    each K step's activation tile once into an LDS ring that all three
+//    waves read. In the layer's own schedule the waves find their expert's
+//    slots in the routing ids; through the standalone entry points they read
+//    offsets / sorted_rows.
 //  * tiled ("wide", many rows per expert: prefill). A 256-thread block owns
 //    four 64-row groups x 64 tokens; the gathered activation tile goes
 //    through a double-buffered LDS ring (128 K per step), weights straight to
@@ -129,12 +130,15 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
 // ------------------------------------------------------------------ skinny
 constexpr int kSkBT = 16;      // tokens per tile
 constexpr int kSkDepth = 3;    // prefetch depth in K steps
+constexpr int kSkWaves = 3;    // waves per workgroup: one expert, the activation tile shared
+constexpr int kSkThreads = 64 * kSkWaves;
+constexpr int kSkXStage = kSkBT * 256;       // activation tile of one K step: 16 rows x 128 bf16
+constexpr int kSkXChunks = kSkXStage / 16;   // its 16-byte pieces (256)
+static_assert(kSkXChunks > kSkThreads && kSkXChunks <= 2 * kSkThreads, "two pieces per thread at most");
 
-template <int RG>
 struct SkStage {
-  uint4 w[4 * RG];
-  uint32_t sc[RG];
-  uint4 xv[4];
+  uint4 w[4];    // four 16-row tiles of the wave's group
+  uint32_t sc;   // their four scale bytes
 };
 
 // Position of the n-th set bit (n < popcount) of a 64-bit mask.
@@ -176,19 +180,38 @@ __device__ __forceinline__ void scan_expert_slots(const int32_t* ids, int n, int
   }
 }
 
-// One work item: RG consecutive 64-row groups G0.. of expert e. One wave streams RG groups
-// (64*RG rows: the activations it reads are shared by all of them). The
-// weight stream needs no routing data, so the wave only waits for the
-// expert's row range and its first row lookups before the stream starts; a
-// dependent load issued behind the chip-wide weight traffic would wait for
-// the whole in-flight volume. An expert with more than 16 rows is handled 16
-// at a time.
-template <int EPI, int RG, class WaitAct>
-__device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, const WaitAct& wait_act) {
-  constexpr int MT = 4 * RG;
-  const int lane = threadIdx.x;
+// One workgroup: kSkWaves waves, each streaming one 64-row group of expert
+// e, over the expert's tokens 16 at a time. The
+// weight stream needs no routing data, so a wave only waits for the expert's
+// row range and its first row lookups before the stream starts; a dependent
+// load issued behind the chip-wide weight traffic would wait for the whole
+// in-flight volume. The weights are read once and loaded non-temporally.
+// The activations of a K step (16 token rows x 256 bytes) are loaded once
+// per workgroup, a 16-byte piece per thread (two for the first wave), written
+// to a 3-slot LDS ring (pieces XOR-swizzled by row) and read back in the
+// matrix-core layout by every wave: per-wave activation loads, though L2
+// hits, cost the weight stream a sixth of its rate.
+template <int EPI>
+__global__ __launch_bounds__(kSkThreads) void ffn_skinny_kernel(FfnArgs a) {
+  constexpr int MT = 4;
+  // the ring, then a spare area for the second pieces of waves 1.. (never read)
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kSkDepth * kSkXStage + kSkThreads * 16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e = blockIdx.y;
+  const int G0 = blockIdx.x * kSkWaves + wave;   // the wave's 64-row group
   const int r = lane & 15;   // weight row in a 16-row tile / token column
   const int g = lane >> 4;   // lane group: MX block 4s + g of step s
+  // activation pieces of this thread: piece c = (token row c >> 4, 16-byte
+  // piece c & 15 of the step's 256 bytes); the second one only in wave 0
+  // (the other waves load their first piece again and write it to the spare
+  // area, so the code has no branch)
+  const int c0 = tid;
+  const int c1 = wave == 0 ? tid + kSkThreads : tid;
+  const int xw0 = (c0 >> 4) * 256 + (((c0 & 15) ^ (c0 >> 4)) & 15) * 16;
+  const int xw1 = wave == 0 ? (c1 >> 4) * 256 + (((c1 & 15) ^ (c1 >> 4)) & 15) * 16 : -1;
+
   int e_begin, e_end, slot_first = -1;
   if (a.ids) {
     int below, count;
@@ -199,7 +222,7 @@ __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, con
     e_begin = a.offsets[e];
     e_end = a.offsets[e + 1];
   }
-  if (e_end <= e_begin) return;
+  if (e_end <= e_begin) return;   // the whole workgroup: one expert
   // biases of this lane's output rows (consumed by the epilogue)
   const uint16_t* bias = a.bias + (size_t)e * a.N + G0 * 64 + 4 * g;
   uint2 braw[MT];
@@ -226,47 +249,38 @@ __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, con
     // the routing weight is fetched with the row lookups, not behind the stream
     float wt = 0.f;
     if constexpr (EPI == EPI_COMBINE) wt = a.topk_w[slot];
-    const int arow = a.gather ? slot / a.k : (tok_ok ? p : rb);
-    const uint16_t* xp = a.act + (size_t)arow * kH;
+    // activation rows of this thread's pieces (token rows c >> 4 of the tile)
+    const int tr0 = c0 >> 4, tr1 = (c1 >> 4) & 15;
+    const int slot0 = __shfl(slot, tr0, 64), slot1 = __shfl(slot, tr1, 64);
+    const int arow0 = a.gather ? slot0 / a.k : (rb + tr0 < re ? rb + tr0 : rb);
+    const int arow1 = a.gather ? slot1 / a.k : (rb + tr1 < re ? rb + tr1 : rb);
+    const uint16_t* xp0 = a.act + (size_t)arow0 * kH + (c0 & 15) * 8;
+    const uint16_t* xp1 = a.act + (size_t)arow1 * kH + (c1 & 15) * 8;
     // slot >= 0 always; the compiler cannot know it, so the weight addresses
     // depend on the row lookup and the stream starts after it returns
-    GroupStream ws[RG];
-#pragma unroll
-    for (int q = 0; q < RG; ++q) ws[q].init(a, e + (slot < 0 ? 1 : 0), G0 + q, lane);
+    GroupStream ws;
+    ws.init(a, e + (slot < 0 ? 1 : 0), G0, lane);
 
     // s is a compile-time constant after unrolling; the K tail (blocks >= 90)
-    // re-reads block 89, whose weights are zero there
-    auto issue_w = [&](SkStage<RG>& st, int s) __attribute__((always_inline)) {
-#pragma unroll
-      for (int q = 0; q < RG; ++q) {
-        uint4 w4[4];
-        ws[q].template load<true>(s, w4, st.sc[q]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) st.w[4 * q + mt] = w4[mt];
-      }
-    };
-    // With one group per wave (the down projection) only the lanes of real
-    // token columns load: a decode tile is often half empty. Measured on the
-    // two-group wave (gate/up) the branch costs more than the loads it saves.
-    auto issue_x = [&](SkStage<RG>& st, int s) __attribute__((always_inline)) {
-      const int kb = min(4 * s + g, kKB - 1);
-      if (RG > 1 || tok_ok) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st.xv[i] = *reinterpret_cast<const uint4*>(xp + kb * 32 + 8 * i);
-      }
+    // re-reads the row's last 8 values, whose weights are zero there
+    auto issue = [&](SkStage& st, u32x4& x0, u32x4& x1, int s) __attribute__((always_inline)) {
+      ws.template load<true>(s, st.w, st.sc);
+      const int k0 = s * 128;
+      x0 = *reinterpret_cast<const u32x4*>(xp0 + min(k0, kH - 8 - (c0 & 15) * 8));
+      x1 = *reinterpret_cast<const u32x4*>(xp1 + min(k0, kH - 8 - (c1 & 15) * 8));
     };
 
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const SkStage<RG>& st) __attribute__((always_inline)) {
+    auto compute = [&](const SkStage& st, const uint8_t* xsb) __attribute__((always_inline)) {
       float sf[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) sf[mt] = e8m0_to_f32((st.sc[mt / 4] >> (8 * (mt % 4))) & 0xFFu);
+      for (int mt = 0; mt < MT; ++mt) sf[mt] = e8m0_to_f32((st.sc >> (8 * mt)) & 0xFFu);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16x8 xb = u4_as_bf16x8(st.xv[i]);
+        const bf16x8 xb = *reinterpret_cast<const bf16x8*>(xsb + r * 256 + (((4 * g + i) ^ r) & 15) * 16);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const bf16x8 wb = fp4x8_to_bf16x8(dword_of(st.w[mt], i), sf[mt]);
@@ -275,27 +289,27 @@ __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, con
       }
     };
 
-    // fully unrolled K loop with a kSkDepth-step register prefetch ring
-    // (the first weight stages go out before the activations may be read)
-    SkStage<RG> st[kSkDepth];
-    if constexpr (RG == 1) {
+    // fully unrolled K loop with a kSkDepth-step register prefetch ring; per
+    // step: write this thread's activation pieces into the step's LDS slot,
+    // wait for the LDS writes, barrier, then every wave computes from LDS and
+    // refills the ring slot. A slot is rewritten kSkDepth steps after it was
+    // read, and its readers have passed the barrier in between.
+    SkStage st[kSkDepth];
+    u32x4 x0[kSkDepth], x1[kSkDepth];
 #pragma unroll
-      for (int q = 0; q < kSkDepth; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[q].xv[i] = make_uint4(0u, 0u, 0u, 0u);   // empty token columns
-    }
-#pragma unroll
-    for (int q = 0; q < kSkDepth; ++q) issue_w(st[q], q);
-    if (rb == e_begin) wait_act();
-#pragma unroll
-    for (int q = 0; q < kSkDepth; ++q) issue_x(st[q], q);
+    for (int q = 0; q < kSkDepth; ++q) issue(st[q], x0[q], x1[q], q);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      compute(st[s % kSkDepth]);
-      if (s + kSkDepth < kSteps) {
-        issue_w(st[s % kSkDepth], s + kSkDepth);
-        issue_x(st[s % kSkDepth], s + kSkDepth);
-      }
+      const int q = s % kSkDepth;
+      const int xo = q * kSkXStage;
+      *reinterpret_cast<u32x4*>(xs + xo + xw0) = x0[q];
+      *reinterpret_cast<u32x4*>(xs + (xw1 >= 0 ? xo + xw1 : kSkDepth * kSkXStage + tid * 16)) = x1[q];
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this thread's LDS writes are done
+      __builtin_amdgcn_s_barrier();
+      compute(st[q], xs + xo);
+      if (s + kSkDepth < kSteps) issue(st[q], x0[q], x1[q], s + kSkDepth);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // 16x16 result: lane holds token column r and weight rows 4g + j of each tile.
@@ -325,26 +339,14 @@ __device__ __forceinline__ void skinny_item(const FfnArgs& a, int G0, int e, con
   }
 }
 
-struct NoWait {
-  __device__ void operator()() const {}
-};
-
-// Grid (RG-group items, expert e).
-template <int EPI, int RG>
-__global__ __launch_bounds__(64) void ffn_skinny_kernel(FfnArgs a) {
-  skinny_item<EPI, RG>(a, blockIdx.x * RG, blockIdx.y, NoWait{});
-}
-
-// Two groups per wave halve the activation reads per weight byte, but only
-// pay off while enough waves remain in flight: the gate/up GEMM (90 groups
-// per expert) takes two, the down GEMM (45) one.
+// Grid (workgroups of kSkWaves groups, expert): 30 workgroups per expert for
+// the gate/up GEMM (90 groups), 15 for the down GEMM (45).
 template <int EPI>
-static void launch_skinny(const FfnArgs& a, hipStream_t s) {
+static hipError_t launch_skinny(const FfnArgs& a, hipStream_t s) {
   const int groups = a.N >> 6;
-  if (groups % 2 == 0 && groups >= 90)
-    hipLaunchKernelGGL((ffn_skinny_kernel<EPI, 2>), dim3(groups / 2, a.E), dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL((ffn_skinny_kernel<EPI, 1>), dim3(groups, a.E), dim3(64), 0, s, a);
+  if (groups % kSkWaves != 0) return hipErrorInvalidValue;   // every wave owns one group
+  hipLaunchKernelGGL((ffn_skinny_kernel<EPI>), dim3(groups / kSkWaves, a.E), dim3(kSkThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ wide
@@ -649,9 +651,9 @@ hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s)
   const bool skinny = !a.act6 && !ffn_uses_tiles(n_rows, a.E);   // records: tiled only
   if (skinny) {
     switch (epi) {
-      case EPI_SWIGLU: launch_skinny<EPI_SWIGLU>(a, s); break;
-      case EPI_COMBINE: launch_skinny<EPI_COMBINE>(a, s); break;
-      default: launch_skinny<EPI_STORE_Y>(a, s); break;
+      case EPI_SWIGLU: return launch_skinny<EPI_SWIGLU>(a, s);
+      case EPI_COMBINE: return launch_skinny<EPI_COMBINE>(a, s);
+      default: return launch_skinny<EPI_STORE_Y>(a, s);
     }
   } else {
     const int tiles = (n_rows + kWdBT - 1) / kWdBT + min(a.E, n_rows);
