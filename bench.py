@@ -72,6 +72,43 @@ def measured_traffic(workload: str):
     return ent.get("traffic_bytes")
 
 
+def measured_peaks(dev):
+    """Reference rates measured on this device in the same run (not part of
+    the layer): a 2 GiB device-to-device copy through torch (bytes read +
+    written per second) and a 8192^3 bf16 matrix product through torch
+    (hipBLASLt). The roofline fractions are also given against these."""
+    import torch
+    n = (2 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * 4 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 2.0 * m ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tf, 1),
+            "how": "torch device copy of 2 GiB (read + write bytes); torch bf16 8192^3 matmul"}
+
+
 def cpu_baseline(inp, cfg, n_tokens):
     import numpy as np
     import oracle
@@ -105,6 +142,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0,
                     help="device copies of the weights to rotate over (0: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peak-probe", action="store_true",
+                    help="skip the reference copy / matrix-product rates")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle sample (0: automatic)")
     ap.add_argument("--path", choices=("bf16", "mx6"), default="bf16",
@@ -332,6 +371,15 @@ def main() -> int:
         "step_ms_p10_p50_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
         "ms_per_step_one_weight_copy": None if nonrot_ms is None else round(nonrot_ms, 5),
     }
+    if not args.no_peak_probe:
+        peaks = measured_peaks(dev)
+        res["measured_peaks"] = peaks
+        if roof["unit"] == "GB/s":
+            roof["frac_of_measured_copy"] = round(roof["achieved"] / peaks["hbm_copy_GBps"], 4)
+        elif not mx6:
+            roof["frac_of_measured_gemm"] = round(roof["achieved"] / peaks["bf16_gemm_TFLOPs"], 4)
+        else:
+            roof["bf16_equivalent_frac_of_measured_gemm"] = round(roof["achieved"] / peaks["bf16_gemm_TFLOPs"], 4)
     if not args.no_cpu_baseline:
         n = args.cpu_tokens or (cfg.T if cfg.T <= 64 else (32 if E <= 32 else 16))
         log(f"bench: oracle on {n} tokens")
