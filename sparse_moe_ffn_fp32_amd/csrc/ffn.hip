@@ -640,10 +640,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
 }
 
 // ------------------------------------------------------------------ dispatch
-constexpr int kSkinnyMaxMeanRows = 24;
+// Largest mean routed rows per expert (T*k / E) for the weight-streaming
+// schedule. Measured layer crossovers against the tiled schedule: about 20
+// rows at E = 8 and E = 32, 12-16 at E = 128, 8-12 at E = 256 (with more
+// experts more of them exceed one 16-row tile and stream their weights again).
+int skinny_max_mean_rows(int E) { return E <= 32 ? 16 : (E <= 128 ? 12 : 8); }
 
 bool ffn_uses_tiles(int n_rows, int E) {
-  return (long long)n_rows > (long long)kSkinnyMaxMeanRows * E;
+  return (long long)n_rows > (long long)skinny_max_mean_rows(E) * E;
 }
 
 hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s) {

@@ -130,21 +130,23 @@ def test_permute(T, E, k):
 
 
 # ---------------------------------------------------------------- experts
-# (T, E, k): T*k <= 24*E takes the weight-streaming kernel, above it the tiled one
+# (T, E, k): few rows per expert (T*k <= 16*E at E <= 32, 12*E at E <= 128)
+# take the weight-streaming kernel, more the tiled one
 SMALL_CASES = [
     (1, 1, 1),      # one expert: every slot goes to it with weight 1
-    (33, 1, 1),     # the same past the schedule threshold (33 > 24 rows): tiled
-    (48, 8, 4),     # T*k = 24*E exactly: the last weight-streaming shape
-    (49, 8, 4),     # one token more: the first tiled one
+    (33, 1, 1),     # the same past the schedule threshold (33 > 16 rows): tiled
+    (32, 8, 4),     # T*k = 16*E exactly: the last weight-streaming shape
+    (33, 8, 4),     # one token more: the first tiled one
     (1, 4, 4),      # every expert selected
     (5, 8, 2),
     (16, 32, 4),    # the 20b T=16 shape
-    (40, 8, 4),     # experts with more than one 16-row tile
+    (30, 8, 4),     # weight streaming with experts of more than one 16-row tile
+    (40, 8, 4),
     (130, 4, 4),    # tiled: 128-row tile + ragged tail
     (300, 4, 1),    # tiled, k = 1
     (256, 8, 4),
-    (192, 32, 4),   # weight-streaming kernels behind the many-token router (T > 128)
-    (300, 64, 4),   # the same with two expert tiles in the router
+    (192, 64, 4),   # weight-streaming kernels behind the many-token router (T > 128)
+    (300, 64, 4),   # tiled, two expert tiles in the router
 ]
 
 
