@@ -48,6 +48,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
 
 // operand format codes of the f8f6f4 matrix-core instructions
 constexpr int kFmtE2M3 = 2;
@@ -193,12 +195,47 @@ __device__ __forceinline__ void mx6_encode_piece(const float (&v)[32], uint32_t 
   scale = (uint32_t)(X + 127);
 }
 
+// The same piece on CDNA4's scaled conversion instructions: the 32 values
+// divided by 2^X and rounded to E2M3 (nearest even, saturating) in one
+// instruction, whose two 16-value operands are interleaved in its output
+// (output j = operand a[j/2] for even j, b[j/2] for odd j), and the piece's
+// values back by the inverse conversion. Returns false, leaving the outputs
+// unset, when 2^X or the piece's smallest values would not be normal floats
+// (X < -120): the caller then takes the arithmetic path above. Bit for bit
+// the same codes as mx6_encode_piece for every input but -0.0, which the
+// instruction encodes with its sign bit set (callers pass +0.0).
+__device__ __forceinline__ bool mx6_encode_piece_cvt(const float (&v)[32], uint32_t (&w)[6],
+                                                     uint32_t& scale, float (&res)[32]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const int X = mx6_shared_exp(amax);
+  if (X < -120) return false;
+  const float sc = ldexpf(1.0f, X);
+  f32x16 a, b;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    a[i] = v[2 * i];
+    b[i] = v[2 * i + 1];
+  }
+  const u32x6 c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, sc);
+  const f32x32 q = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, sc);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) w[i] = c[i];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) res[j] = v[j] - q[j];
+  scale = (uint32_t)(X + 127);
+  return true;
+}
+
 // Both pieces of a 32-value block.
 __device__ __forceinline__ void mx6x2_encode(const float (&v)[32], uint32_t (&w1)[6], uint32_t& s1,
                                              uint32_t (&w2)[6], uint32_t& s2) {
-  float r1[32], r2[32];
-  mx6_encode_piece(v, w1, s1, r1);
-  mx6_encode_piece(r1, w2, s2, r2);
+  float v0[32], r1[32], r2[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v0[j] = v[j] + 0.0f;   // -0.0 -> +0.0
+  if (!mx6_encode_piece_cvt(v0, w1, s1, r1)) mx6_encode_piece(v0, w1, s1, r1);
+  if (!mx6_encode_piece_cvt(r1, w2, s2, r2)) mx6_encode_piece(r1, w2, s2, r2);
 }
 
 }  // namespace moe
