@@ -21,7 +21,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t ids, w, counts, offsets, sorted, scratch, h, y, xrec, xnorm, total;
+  size_t ids, w, counts, offsets, sorted, scratch, h, y, xrec, xnorm, hrec, total;
 };
 
 bool sizes_ok(int T, int E, int k) {
@@ -49,6 +49,9 @@ WsLayout layout(int T, int E, int k) {
   if (tiles) off = align_up(off + (size_t)T * moe::kRowRecBytes);
   // moe_forward_block: the normed bf16 input of the layer
   l.xnorm = off;    off = align_up(off + (size_t)T * moe::kH * 2);
+  // moe_forward_mx6, tiled schedule: h as two-piece MX FP6 records
+  l.hrec = off;
+  if (tiles) off = align_up(off + n * (size_t)moe::kRowRecBytes);
   l.total = off;
   return l;
 }
@@ -359,6 +362,11 @@ moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
   // served far from the CUs at a fraction of the store rate.
   float* y = reinterpret_cast<float*>(base + l.y);
   a2.y_out = y;
+  if (tiles && mx6) {   // records exist (and have workspace) for the tiled schedule only
+    uint8_t* hrec = reinterpret_cast<uint8_t*>(base + l.hrec);
+    MOE_TRY(after_launch(moe::launch_mx6_encode(h, n, hrec, s), s));
+    a2.act6 = hrec;
+  }
   MOE_TRY(after_launch(moe::launch_ffn(a2, moe::EPI_STORE_Y, n, s), s));
   return after_launch(moe::launch_combine(y, w, T, k, resid, out, s), s);
 }
