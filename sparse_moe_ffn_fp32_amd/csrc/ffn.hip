@@ -581,6 +581,61 @@ __device__ __forceinline__ void wide_body(const FfnArgs& a) {
       }
     }
   }
+  if constexpr (MX6 && !W_AS_B && EPI == EPI_SWIGLU) {
+    if (a.h6_out) {
+      // h as two-piece MX FP6 records: this wave's 32 h features of a token
+      // (group G of 64 interleaved gate/up rows) are MX block G of that
+      // token's h row, i.e. block G % 4 of the record of K step G / 4. The
+      // wave's bf16 h values go token-major through its own 4 KiB of LDS
+      // stage 1 (idle since the last step's barrier; LDS operations of a wave
+      // complete in order), then lane t encodes token t's block, the same
+      // rounding to bf16 first as the separate encoder. The waves past the
+      // last group (G = 90, 91) write the zero blocks that pad the last step.
+      const int t = lane;
+      const int p = rb + t;
+      const int st = G >> 2, gb = G & 3;
+      uint8_t* rec = a.h6_out + (size_t)p * kRowRecBytes + st * kRecBytes;
+      uint32_t w1[6], w2[6], s1 = 127u, s2 = 127u;
+#pragma unroll
+      for (int i = 0; i < 6; ++i) w1[i] = w2[i] = 0u;
+      if (w_ok) {
+        uint8_t* hs = xs + kXStage + wave * (kWdBT * 64);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          float b[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b[j] = bf16_bits_to_f32(bias_s[wave * 64 + 16 * mt + 4 * g + j]);
+#pragma unroll
+          for (int nt = 0; nt < kWdNT; ++nt) {
+            const f32x4& c = acc[mt][nt];
+            const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(c[0] + b[0], c[1] + b[1]));
+            const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(c[2] + b[2], c[3] + b[3]));
+            *reinterpret_cast<uint32_t*>(hs + (16 * nt + r) * 64 + (8 * mt + 2 * g) * 2) = h0 | (h1 << 16);
+          }
+        }
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 d = *reinterpret_cast<const uint4*>(hs + t * 64 + q * 16);
+          const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[8 * q + 2 * i] = bf16_bits_to_f32(dw[i] & 0xFFFFu);
+            v[8 * q + 2 * i + 1] = bf16_bits_to_f32(dw[i] >> 16);
+          }
+        }
+        mx6x2_encode(v, w1, s1, w2, s2);
+      }
+      if (p < re) {
+        *reinterpret_cast<uint4*>(rec + gb * 16) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        *reinterpret_cast<uint4*>(rec + (4 + gb) * 16) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+        *reinterpret_cast<uint2*>(rec + (8 + (gb >> 1)) * 16 + (gb & 1) * 8) = make_uint2(w1[4], w1[5]);
+        *reinterpret_cast<uint2*>(rec + (10 + (gb >> 1)) * 16 + (gb & 1) * 8) = make_uint2(w2[4], w2[5]);
+        *reinterpret_cast<uint16_t*>(rec + 12 * 16 + 2 * gb) = (uint16_t)(s1 | (s2 << 8));
+      }
+      return;
+    }
+  }
   if (!w_ok) return;
 
   if constexpr (!W_AS_B) {

@@ -346,9 +346,12 @@ moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
     a13.ids = ids;
     a13.n_slots = n;
   } else if (mx6) {
+    // x and h as two-piece MX FP6 records: x by the encoder, h by the
+    // gate/up epilogue, for the block-scaled matrix cores of both GEMMs
     uint8_t* xrec = reinterpret_cast<uint8_t*>(base + l.xrec);
     MOE_TRY(after_launch(moe::launch_mx6_encode(x, T, xrec, s), s));
     a13.act6 = xrec;
+    a13.h6_out = reinterpret_cast<uint8_t*>(base + l.hrec);
   }
   MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));
   FfnArgs a2 = ffn_args(h, offsets, sorted, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
@@ -362,11 +365,7 @@ moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
   // served far from the CUs at a fraction of the store rate.
   float* y = reinterpret_cast<float*>(base + l.y);
   a2.y_out = y;
-  if (tiles && mx6) {   // records exist (and have workspace) for the tiled schedule only
-    uint8_t* hrec = reinterpret_cast<uint8_t*>(base + l.hrec);
-    MOE_TRY(after_launch(moe::launch_mx6_encode(h, n, hrec, s), s));
-    a2.act6 = hrec;
-  }
+  if (tiles && mx6) a2.act6 = reinterpret_cast<uint8_t*>(base + l.hrec);   // written by the gate/up epilogue
   MOE_TRY(after_launch(moe::launch_ffn(a2, moe::EPI_STORE_Y, n, s), s));
   return after_launch(moe::launch_combine(y, w, T, k, resid, out, s), s);
 }

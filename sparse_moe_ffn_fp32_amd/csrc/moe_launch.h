@@ -36,6 +36,10 @@ struct FfnArgs {
   // two-piece MX FP6 records ([rows, 23 steps, 256 B], moe_device.h) through
   // the block-scaled FP4 x FP6 matrix-core instruction instead of `act`.
   const uint8_t* act6;
+  // Tiled gate/up on records (EPI_SWIGLU with act6) only: when not null, h is written as two-piece
+  // MX FP6 records [T*k, 23 steps, 256 B] for a block-scaled down projection
+  // instead of bf16 into h_out (the bytes no kernel reads are left unwritten).
+  uint8_t* h6_out;
 };
 
 // Router + top-k + softmax; with `counts` non-null the expert permutation is
