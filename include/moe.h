@@ -202,13 +202,15 @@ moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
  * the MXFP4 weights enter the instruction as they are (their E8M0 scales are
  * the instruction's block scales) and each activation row x[t] is held as
  * two MX FP6 (E2M3) pieces, P1 + P2 (moe_encode_mx6), each multiplied by the
- * weights at the FP4 x FP6 rate. The pieces stand for x[t] to within
- * max|x_block| / 256 per 32-value block; the layer output stays within the
- * accuracy of moe_forward's bf16 matrix-core path while the weight scales of
- * an expert span up to about 16 binades (checkpoint-like weights span a few);
- * past that, use moe_forward. The down projection and the
- * few-rows-per-expert (decode) schedule are those of moe_forward. Arguments,
- * workspace and errors as moe_forward. Source: the pages fix MXFP4 weights
+ * weights at the FP4 x FP6 rate; the down projection takes the gate/up output
+ * h the same way (rounded to bf16, then encoded by the gate/up kernel as it
+ * writes h). The pieces stand for a row to within max|block| / 256 per
+ * 32-value block; the layer output stays within the accuracy bar of
+ * moe_forward while the weight scales of an expert span up to about 16
+ * binades (checkpoint-like weights span a few); past that, use moe_forward.
+ * The few-rows-per-expert (decode) schedule is that of moe_forward.
+ * Arguments and errors as moe_forward; the workspace (moe_workspace_size)
+ * also holds the records of x and h. Source: the pages fix MXFP4 weights
  * and their packing for inference (techniques map, "inference & serving");
  * the piece encoding follows the OCP Microscaling v1.0 conversion and is
  * this library's. */
