@@ -181,11 +181,11 @@ __device__ __forceinline__ void scan_expert_slots(const int32_t* ids, int n, int
 }
 
 // One workgroup: kSkWaves waves, each streaming one 64-row group of expert
-// e, over the expert's tokens 16 at a time. The
-// weight stream needs no routing data, so a wave only waits for the expert's
-// row range and its first row lookups before the stream starts; a dependent
-// load issued behind the chip-wide weight traffic would wait for the whole
-// in-flight volume. The weights are read once and loaded non-temporally.
+// e, over the expert's tokens 16 at a time. The weight stream needs no
+// routing data, so a wave only waits for the expert's row range and its first
+// row lookups before the stream starts; a dependent load issued behind the
+// chip-wide weight traffic would wait for the whole in-flight volume. The
+// weights are read once and loaded non-temporally.
 // The activations of a K step (16 token rows x 256 bytes) are loaded once
 // per workgroup, a 16-byte piece per thread (two for the first wave), written
 // to a 3-slot LDS ring (pieces XOR-swizzled by row) and read back in the
