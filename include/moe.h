@@ -185,7 +185,7 @@ moe_status_t moe_combine(const float* y, const float* topk_w, int T, int k,
 /* The whole layer: route -> permute -> gate/up + SwiGLU -> down projection
  * -> routing-weighted combine (a token's k expert outputs summed in slot
  * order: results are reproducible bit for bit). Few routed rows per expert
- * (T*k <= 16*E for E <= 32, 12*E for E <= 128, else 8*E) take the
+ * (T*k <= 28*E for E <= 32, 20*E for E <= 128, else 10*E) take the
  * weight-streaming schedule, which finds each expert's slots in the routing
  * ids instead of building the permutation.
  * Arguments as above; out [T, 2880] fp32 is overwritten. */

@@ -128,13 +128,19 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
 }
 
 // ------------------------------------------------------------------ skinny
-constexpr int kSkBT = 16;      // tokens per tile
 constexpr int kSkDepth = 3;    // prefetch depth in K steps
+constexpr int kSkTwoTilesMeanRows = 10;   // mean rows per expert above which a pass covers 32 tokens
 constexpr int kSkWaves = 3;    // waves per workgroup: one expert, the activation tile shared
 constexpr int kSkThreads = 64 * kSkWaves;
-constexpr int kSkXStage = kSkBT * 256;       // activation tile of one K step: 16 rows x 128 bf16
-constexpr int kSkXChunks = kSkXStage / 16;   // its 16-byte pieces (256)
-static_assert(kSkXChunks > kSkThreads && kSkXChunks <= 2 * kSkThreads, "two pieces per thread at most");
+
+// One pass over the weights serves NT 16-token column tiles.
+template <int NT>
+struct SkShape {
+  static constexpr int BT = 16 * NT;                  // tokens per pass
+  static constexpr int XStage = BT * 256;             // activation tile of one K step (128 bf16 per row)
+  static constexpr int Pieces = XStage / 16;          // its 16-byte pieces
+  static constexpr int PPT = (Pieces + kSkThreads - 1) / kSkThreads;   // pieces per thread
+};
 
 struct SkStage {
   uint4 w[4];    // four 16-row tiles of the wave's group
@@ -158,16 +164,19 @@ __device__ __forceinline__ int nth_set_bit(unsigned long long m, int n) {
 
 // Expert e's slots straight from the routing ids: `below` = slots of lower
 // experts (e's first position in the stable expert order), `count` = e's
-// slots, and for lane r the slot of rank rank0 + (r & 15) among e's slots in
-// slot order (-1 past the end). One pass of coalesced loads, no dependent
-// lookups; every lane of the wave must call it.
+// slots, and for lane r the slots of ranks rank0 + (r & 15) and rank0 + 16 +
+// (r & 15) among e's slots in slot order (-1 past the end). One pass of
+// coalesced loads, no dependent lookups; every lane of the wave must call it.
 __device__ __forceinline__ void scan_expert_slots(const int32_t* ids, int n, int e, int rank0,
-                                                  int& below, int& count, int& slot_r) {
+                                                  int& below, int& count, int& slot_r,
+                                                  int& slot_r16) {
   const int lane = threadIdx.x & 63;
   const int tr = rank0 + (lane & 15);
+  const int tr16 = tr + 16;
   below = 0;
   count = 0;
   slot_r = -1;
+  slot_r16 = -1;
 #pragma unroll 4
   for (int c = 0; c < n; c += 64) {
     const int i = c + lane;
@@ -176,26 +185,31 @@ __device__ __forceinline__ void scan_expert_slots(const int32_t* ids, int n, int
     below += __popcll(__ballot(id < e));
     const int in = __popcll(eq);
     if (tr >= count && tr < count + in) slot_r = c + nth_set_bit(eq, tr - count);
+    if (tr16 >= count && tr16 < count + in) slot_r16 = c + nth_set_bit(eq, tr16 - count);
     count += in;
   }
 }
 
 // One workgroup: kSkWaves waves, each streaming one 64-row group of expert
-// e, over the expert's tokens 16 at a time. The weight stream needs no
+// e, over the expert's tokens 16 * NT at a time. The weight stream needs no
 // routing data, so a wave only waits for the expert's row range and its first
 // row lookups before the stream starts; a dependent load issued behind the
 // chip-wide weight traffic would wait for the whole in-flight volume. The
 // weights are read once and loaded non-temporally.
-// The activations of a K step (16 token rows x 256 bytes) are loaded once
-// per workgroup, a 16-byte piece per thread (two for the first wave), written
-// to a 3-slot LDS ring (pieces XOR-swizzled by row) and read back in the
+// The activations of a K step (16 * NT token rows x 256 bytes) are loaded
+// once per workgroup, 16-byte pieces spread over the threads, written to a
+// 3-slot LDS ring (pieces XOR-swizzled by row) and read back in the
 // matrix-core layout by every wave: per-wave activation loads, though L2
 // hits, cost the weight stream a sixth of its rate.
-template <int EPI>
+template <int EPI, int NT>
 __global__ __launch_bounds__(kSkThreads) void ffn_skinny_kernel(FfnArgs a) {
+  using Sh = SkShape<NT>;
   constexpr int MT = 4;
-  // the ring, then a spare area for the second pieces of waves 1.. (never read)
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kSkDepth * kSkXStage + kSkThreads * 16];
+  constexpr int PPT = Sh::PPT;
+  // the ring, then a spare area for the pieces a thread has beyond the tile
+  // (it loads its first piece again and writes it there, so the code has no
+  // branch; never read)
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kSkDepth * Sh::XStage + kSkThreads * 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -204,18 +218,20 @@ __global__ __launch_bounds__(kSkThreads) void ffn_skinny_kernel(FfnArgs a) {
   const int r = lane & 15;   // weight row in a 16-row tile / token column
   const int g = lane >> 4;   // lane group: MX block 4s + g of step s
   // activation pieces of this thread: piece c = (token row c >> 4, 16-byte
-  // piece c & 15 of the step's 256 bytes); the second one only in wave 0
-  // (the other waves load their first piece again and write it to the spare
-  // area, so the code has no branch)
-  const int c0 = tid;
-  const int c1 = wave == 0 ? tid + kSkThreads : tid;
-  const int xw0 = (c0 >> 4) * 256 + (((c0 & 15) ^ (c0 >> 4)) & 15) * 16;
-  const int xw1 = wave == 0 ? (c1 >> 4) * 256 + (((c1 & 15) ^ (c1 >> 4)) & 15) * 16 : -1;
+  // piece c & 15 of the row's 256 bytes of the step)
+  int pc[PPT], pw[PPT];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int c = tid + i * kSkThreads;
+    const bool in = c < Sh::Pieces;
+    pc[i] = in ? c : tid;
+    pw[i] = in ? (c >> 4) * 256 + (((c & 15) ^ (c >> 4)) & 15) * 16 : -1;   // at most one spare per thread
+  }
 
-  int e_begin, e_end, slot_first = -1;
+  int e_begin, e_end, slot_first = -1, slot_first16 = -1;
   if (a.ids) {
     int below, count;
-    scan_expert_slots(a.ids, a.n_slots, e, 0, below, count, slot_first);
+    scan_expert_slots(a.ids, a.n_slots, e, 0, below, count, slot_first, slot_first16);
     e_begin = below;
     e_end = below + count;
   } else {
@@ -229,50 +245,64 @@ __global__ __launch_bounds__(kSkThreads) void ffn_skinny_kernel(FfnArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) braw[mt] = *reinterpret_cast<const uint2*>(bias + 16 * mt);
 
-  for (int rb = e_begin; rb < e_end; rb += kSkBT) {
-    const int re = min(e_end, rb + kSkBT);
-    const int p = rb + r;
-    const bool tok_ok = p < re;
-    // padded token columns take the tile's first slot; their outputs are dropped
-    int slot;
+  for (int rb = e_begin; rb < e_end; rb += Sh::BT) {
+    const int re = min(e_end, rb + Sh::BT);
+    // column r of tile nt holds the token of position rb + 16 nt + r; padded
+    // columns take the pass's first slot and their outputs are dropped
+    int slot[NT];
+    bool tok_ok[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) tok_ok[nt] = rb + 16 * nt + r < re;
     if (a.ids) {
-      int sr = slot_first;
+      int sr = slot_first, sr16 = slot_first16;
       if (rb != e_begin) {
         int b2, c2;
-        scan_expert_slots(a.ids, a.n_slots, e, rb - e_begin, b2, c2, sr);
+        scan_expert_slots(a.ids, a.n_slots, e, rb - e_begin, b2, c2, sr, sr16);
       }
-      const int tile_first = __shfl(sr, 0, 64);
-      slot = tok_ok ? sr : tile_first;
+      const int first = __shfl(sr, 0, 64);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) slot[nt] = tok_ok[nt] ? (nt == 0 ? sr : sr16) : first;
     } else {
-      slot = a.sorted_rows[tok_ok ? p : rb];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) slot[nt] = a.sorted_rows[tok_ok[nt] ? rb + 16 * nt + r : rb];
     }
-    // the routing weight is fetched with the row lookups, not behind the stream
-    float wt = 0.f;
-    if constexpr (EPI == EPI_COMBINE) wt = a.topk_w[slot];
-    // activation rows of this thread's pieces (token rows c >> 4 of the tile)
-    const int tr0 = c0 >> 4, tr1 = (c1 >> 4) & 15;
-    const int slot0 = __shfl(slot, tr0, 64), slot1 = __shfl(slot, tr1, 64);
-    const int arow0 = a.gather ? slot0 / a.k : (rb + tr0 < re ? rb + tr0 : rb);
-    const int arow1 = a.gather ? slot1 / a.k : (rb + tr1 < re ? rb + tr1 : rb);
-    const uint16_t* xp0 = a.act + (size_t)arow0 * kH + (c0 & 15) * 8;
-    const uint16_t* xp1 = a.act + (size_t)arow1 * kH + (c1 & 15) * 8;
+    // the routing weights are fetched with the row lookups, not behind the stream
+    float wt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) wt[nt] = EPI == EPI_COMBINE ? a.topk_w[slot[nt]] : 0.f;
+    // activation rows of this thread's pieces (token row c >> 4 of the pass)
+    const uint16_t* xp[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int tr = pc[i] >> 4;
+      int sl = __shfl(slot[0], tr & 15, 64);
+      if (NT > 1) {
+        const int sl16 = __shfl(slot[NT - 1], tr & 15, 64);
+        sl = tr < 16 ? sl : sl16;
+      }
+      const int arow = a.gather ? sl / a.k : (rb + tr < re ? rb + tr : rb);
+      xp[i] = a.act + (size_t)arow * kH + (pc[i] & 15) * 8;
+    }
     // slot >= 0 always; the compiler cannot know it, so the weight addresses
     // depend on the row lookup and the stream starts after it returns
     GroupStream ws;
-    ws.init(a, e + (slot < 0 ? 1 : 0), G0, lane);
+    ws.init(a, e + (slot[0] < 0 ? 1 : 0), G0, lane);
 
     // s is a compile-time constant after unrolling; the K tail (blocks >= 90)
     // re-reads the row's last 8 values, whose weights are zero there
-    auto issue = [&](SkStage& st, u32x4& x0, u32x4& x1, int s) __attribute__((always_inline)) {
+    auto issue = [&](SkStage& st, u32x4 (&xr)[PPT], int s) __attribute__((always_inline)) {
       ws.template load<true>(s, st.w, st.sc);
       const int k0 = s * 128;
-      x0 = *reinterpret_cast<const u32x4*>(xp0 + min(k0, kH - 8 - (c0 & 15) * 8));
-      x1 = *reinterpret_cast<const u32x4*>(xp1 + min(k0, kH - 8 - (c1 & 15) * 8));
+#pragma unroll
+      for (int i = 0; i < PPT; ++i)
+        xr[i] = *reinterpret_cast<const u32x4*>(xp[i] + min(k0, kH - 8 - (pc[i] & 15) * 8));
     };
 
-    f32x4 acc[MT];
+    f32x4 acc[MT][NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](const SkStage& st, const uint8_t* xsb) __attribute__((always_inline)) {
       float sf[MT];
@@ -280,11 +310,16 @@ __global__ __launch_bounds__(kSkThreads) void ffn_skinny_kernel(FfnArgs a) {
       for (int mt = 0; mt < MT; ++mt) sf[mt] = e8m0_to_f32((st.sc >> (8 * mt)) & 0xFFu);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16x8 xb = *reinterpret_cast<const bf16x8*>(xsb + r * 256 + (((4 * g + i) ^ r) & 15) * 16);
+        bf16x8 xb[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          xb[nt] = *reinterpret_cast<const bf16x8*>(xsb + (16 * nt + r) * 256 + (((4 * g + i) ^ r) & 15) * 16);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const bf16x8 wb = fp4x8_to_bf16x8(dword_of(st.w[mt], i), sf[mt]);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb, acc[mt], 0, 0, 0);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xb[nt], acc[mt][nt], 0, 0, 0);
         }
       }
     };
@@ -295,44 +330,49 @@ __global__ __launch_bounds__(kSkThreads) void ffn_skinny_kernel(FfnArgs a) {
     // refills the ring slot. A slot is rewritten kSkDepth steps after it was
     // read, and its readers have passed the barrier in between.
     SkStage st[kSkDepth];
-    u32x4 x0[kSkDepth], x1[kSkDepth];
+    u32x4 xr[kSkDepth][PPT];
 #pragma unroll
-    for (int q = 0; q < kSkDepth; ++q) issue(st[q], x0[q], x1[q], q);
+    for (int q = 0; q < kSkDepth; ++q) issue(st[q], xr[q], q);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const int q = s % kSkDepth;
-      const int xo = q * kSkXStage;
-      *reinterpret_cast<u32x4*>(xs + xo + xw0) = x0[q];
-      *reinterpret_cast<u32x4*>(xs + (xw1 >= 0 ? xo + xw1 : kSkDepth * kSkXStage + tid * 16)) = x1[q];
+      const int xo = q * Sh::XStage;
+#pragma unroll
+      for (int i = 0; i < PPT; ++i)
+        *reinterpret_cast<u32x4*>(xs + (pw[i] >= 0 ? xo + pw[i] : kSkDepth * Sh::XStage + tid * 16)) = xr[q][i];
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this thread's LDS writes are done
       __builtin_amdgcn_s_barrier();
       compute(st[q], xs + xo);
-      if (s + kSkDepth < kSteps) issue(st[q], x0[q], x1[q], s + kSkDepth);
+      if (s + kSkDepth < kSteps) issue(st[q], xr[q], s + kSkDepth);
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // 16x16 result: lane holds token column r and weight rows 4g + j of each tile.
-    if (tok_ok) {
+    // 16x16 results: lane holds token column r of tile nt and weight rows
+    // 4g + j of each weight tile mt.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (!tok_ok[nt]) continue;
+      const int p = rb + 16 * nt + r;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int R0 = G0 * 64 + 16 * mt + 4 * g;
-        const float v0 = acc[mt][0] + bf16_bits_to_f32(braw[mt].x & 0xFFFFu);
-        const float v1 = acc[mt][1] + bf16_bits_to_f32(braw[mt].x >> 16);
-        const float v2 = acc[mt][2] + bf16_bits_to_f32(braw[mt].y & 0xFFFFu);
-        const float v3 = acc[mt][3] + bf16_bits_to_f32(braw[mt].y >> 16);
+        const float v0 = acc[mt][nt][0] + bf16_bits_to_f32(braw[mt].x & 0xFFFFu);
+        const float v1 = acc[mt][nt][1] + bf16_bits_to_f32(braw[mt].x >> 16);
+        const float v2 = acc[mt][nt][2] + bf16_bits_to_f32(braw[mt].y & 0xFFFFu);
+        const float v3 = acc[mt][nt][3] + bf16_bits_to_f32(braw[mt].y >> 16);
         if constexpr (EPI == EPI_SWIGLU) {
           const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(v0, v1));
           const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(v2, v3));
           *reinterpret_cast<uint32_t*>(a.h_out + (size_t)p * kI + R0 / 2) = h0 | (h1 << 16);
         } else if constexpr (EPI == EPI_COMBINE) {
-          float* o = a.out + (size_t)(slot / a.k) * kH + R0;
-          unsafeAtomicAdd(o + 0, wt * v0);
-          unsafeAtomicAdd(o + 1, wt * v1);
-          unsafeAtomicAdd(o + 2, wt * v2);
-          unsafeAtomicAdd(o + 3, wt * v3);
+          float* o = a.out + (size_t)(slot[nt] / a.k) * kH + R0;
+          unsafeAtomicAdd(o + 0, wt[nt] * v0);
+          unsafeAtomicAdd(o + 1, wt[nt] * v1);
+          unsafeAtomicAdd(o + 2, wt[nt] * v2);
+          unsafeAtomicAdd(o + 3, wt[nt] * v3);
         } else {
-          *reinterpret_cast<float4*>(a.y_out + (size_t)slot * kH + R0) = make_float4(v0, v1, v2, v3);
+          *reinterpret_cast<float4*>(a.y_out + (size_t)slot[nt] * kH + R0) = make_float4(v0, v1, v2, v3);
         }
       }
     }
@@ -340,12 +380,17 @@ __global__ __launch_bounds__(kSkThreads) void ffn_skinny_kernel(FfnArgs a) {
 }
 
 // Grid (workgroups of kSkWaves groups, expert): 30 workgroups per expert for
-// the gate/up GEMM (90 groups), 15 for the down GEMM (45).
+// the gate/up GEMM (90 groups), 15 for the down GEMM (45). Two token tiles
+// per pass once most experts have more than 16 rows.
 template <int EPI>
-static hipError_t launch_skinny(const FfnArgs& a, hipStream_t s) {
+static hipError_t launch_skinny(const FfnArgs& a, int n_rows, hipStream_t s) {
   const int groups = a.N >> 6;
   if (groups % kSkWaves != 0) return hipErrorInvalidValue;   // every wave owns one group
-  hipLaunchKernelGGL((ffn_skinny_kernel<EPI>), dim3(groups / kSkWaves, a.E), dim3(kSkThreads), 0, s, a);
+  const dim3 grid(groups / kSkWaves, a.E);
+  if ((long long)n_rows > (long long)kSkTwoTilesMeanRows * a.E)
+    hipLaunchKernelGGL((ffn_skinny_kernel<EPI, 2>), grid, dim3(kSkThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((ffn_skinny_kernel<EPI, 1>), grid, dim3(kSkThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -696,10 +741,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
 
 // ------------------------------------------------------------------ dispatch
 // Largest mean routed rows per expert (T*k / E) for the weight-streaming
-// schedule. Measured layer crossovers against the tiled schedule: about 20
-// rows at E = 8 and E = 32, 12-16 at E = 128, 8-12 at E = 256 (with more
-// experts more of them exceed one 16-row tile and stream their weights again).
-int skinny_max_mean_rows(int E) { return E <= 32 ? 16 : (E <= 128 ? 12 : 8); }
+// schedule (two 16-token tiles per pass above 10 rows). Measured layer
+// crossovers against the tiled schedule: about 28 rows at E = 8 and E = 32,
+// 20 at E = 128, 10 at E = 256 (with more experts more of them exceed one
+// pass and stream their weights again).
+int skinny_max_mean_rows(int E) { return E <= 32 ? 28 : (E <= 128 ? 20 : 10); }
 
 bool ffn_uses_tiles(int n_rows, int E) {
   return (long long)n_rows > (long long)skinny_max_mean_rows(E) * E;
@@ -710,9 +756,9 @@ hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s)
   const bool skinny = !a.act6 && !ffn_uses_tiles(n_rows, a.E);   // records: tiled only
   if (skinny) {
     switch (epi) {
-      case EPI_SWIGLU: return launch_skinny<EPI_SWIGLU>(a, s);
-      case EPI_COMBINE: return launch_skinny<EPI_COMBINE>(a, s);
-      default: return launch_skinny<EPI_STORE_Y>(a, s);
+      case EPI_SWIGLU: return launch_skinny<EPI_SWIGLU>(a, n_rows, s);
+      case EPI_COMBINE: return launch_skinny<EPI_COMBINE>(a, n_rows, s);
+      default: return launch_skinny<EPI_STORE_Y>(a, n_rows, s);
     }
   } else {
     const int tiles = (n_rows + kWdBT - 1) / kWdBT + min(a.E, n_rows);

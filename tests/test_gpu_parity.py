@@ -130,23 +130,27 @@ def test_permute(T, E, k):
 
 
 # ---------------------------------------------------------------- experts
-# (T, E, k): few rows per expert (T*k <= 16*E at E <= 32, 12*E at E <= 128)
-# take the weight-streaming kernel, more the tiled one
+# (T, E, k): few rows per expert (T*k <= 28*E at E <= 32, 20*E at E <= 128;
+# one 16-token tile per pass up to 10 rows on average, two above) take the
+# weight-streaming kernel, more the tiled one
 SMALL_CASES = [
     (1, 1, 1),      # one expert: every slot goes to it with weight 1
-    (33, 1, 1),     # the same past the schedule threshold (33 > 16 rows): tiled
-    (32, 8, 4),     # T*k = 16*E exactly: the last weight-streaming shape
-    (33, 8, 4),     # one token more: the first tiled one
+    (33, 1, 1),     # the same past the schedule threshold (33 > 28 rows): tiled
+    (56, 8, 4),     # T*k = 28*E exactly: the last weight-streaming shape (32-token passes)
+    (57, 8, 4),     # one token more: the first tiled one
     (1, 4, 4),      # every expert selected
     (5, 8, 2),
     (16, 32, 4),    # the 20b T=16 shape
-    (30, 8, 4),     # weight streaming with experts of more than one 16-row tile
-    (40, 8, 4),
+    (40, 16, 4),    # mean 10 rows: the last shape with 16-token passes
+    (44, 16, 4),    # mean 11 rows: the first with 32-token passes
+    (30, 8, 4),     # 32-token passes
+    (40, 8, 4),     # 32-token passes, experts of more than one pass
     (130, 4, 4),    # tiled: 128-row tile + ragged tail
     (300, 4, 1),    # tiled, k = 1
     (256, 8, 4),
     (192, 64, 4),   # weight-streaming kernels behind the many-token router (T > 128)
-    (300, 64, 4),   # tiled, two expert tiles in the router
+    (300, 64, 4),   # the same with two expert tiles in the router
+    (600, 64, 4),   # tiled, E = 64
 ]
 
 
