@@ -318,7 +318,7 @@ def test_forward_config_sampled(idx):
     say(f"  sampled metrics {m}; fused vs unfused {m_all}; near-tie tokens with another set: {n_tie}")
 
 
-@pytest.mark.parametrize("T,E,k", [(16, 32, 4), (256, 8, 4)])
+@pytest.mark.parametrize("T,E,k", [(16, 32, 4), (30, 8, 4), (256, 8, 4)])
 def test_gate_up_and_down_accumulate_onto_residual(T, E, k):
     """The two halves as separate calls; the down half adds into a residual."""
     say(f"gate_up + down_accumulate T={T} E={E} k={k}")
