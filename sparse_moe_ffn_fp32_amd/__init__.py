@@ -63,8 +63,14 @@ _F32 = (torch.float32,)
 _I32 = (torch.int32,)
 
 
-def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+def _stream(*ts: Optional[torch.Tensor]):
+    """The current stream of the device every given tensor lives on (one
+    device per call: the kernels read all their arguments from it)."""
+    dev = ts[0].device
+    for t in ts[1:]:
+        if t is not None and t.device != dev:
+            raise ValueError(f"all tensors of a call must be on one device: {t.device} != {dev}")
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
 def workspace_size(T: int, E: int, k: int) -> int:
@@ -103,7 +109,7 @@ def pack_weights(codes: torch.Tensor, scales: torch.Tensor):
     pc = torch.empty_like(codes)
     ps = torch.empty_like(scales)
     _check(_native.lib().moe_pack_weights(_ptr(codes), _ptr(scales), E, N, _ptr(pc), _ptr(ps),
-                                          _stream(codes)), "moe_pack_weights")
+                                          _stream(codes, scales)), "moe_pack_weights")
     return pc, ps
 
 
@@ -130,7 +136,8 @@ def route(x: torch.Tensor, Wr: torch.Tensor, br: torch.Tensor, k: int = 4,
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if return_logits else None
     ws = _workspace(T, E, k, x.device, workspace)
     _check(_native.lib().moe_route(_ptr(x), _ptr(Wr), _ptr(br), T, E, k, _ptr(ids), _ptr(w),
-                                   _ptr(logits), _ptr(ws), ws.numel(), _stream(x)), "moe_route")
+                                   _ptr(logits), _ptr(ws), ws.numel(),
+                                   _stream(x, Wr, br, ids, w, ws)), "moe_route")
     return (ids, w, logits) if return_logits else (ids, w)
 
 
@@ -144,7 +151,7 @@ def permute(topk_ids: torch.Tensor, E: int, workspace: Optional[torch.Tensor] = 
     rows = torch.empty(T * k, dtype=torch.int32, device=dev)
     ws = _workspace(T, E, k, dev, workspace)
     _check(_native.lib().moe_permute(_ptr(topk_ids), T, E, k, _ptr(counts), _ptr(offsets),
-                                     _ptr(rows), _ptr(ws), ws.numel(), _stream(topk_ids)),
+                                     _ptr(rows), _ptr(ws), ws.numel(), _stream(topk_ids, ws)),
            "moe_permute")
     return counts, offsets, rows
 
@@ -162,7 +169,8 @@ def expert_ffn(x, offsets, sorted_rows, w13_codes, w13_scales, b13, w2_codes, w2
     _check(_native.lib().moe_expert_ffn(
         _ptr(x), _ptr(offsets), _ptr(sorted_rows), _ptr(w13_codes), _ptr(w13_scales), _ptr(b13),
         _ptr(w2_codes), _ptr(w2_scales), _ptr(b2), T, E, k, _ptr(y), _ptr(ws), ws.numel(),
-        _stream(x)), "moe_expert_ffn")
+        _stream(x, offsets, sorted_rows, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, ws)),
+        "moe_expert_ffn")
     return y
 
 
@@ -184,7 +192,8 @@ def gate_up(x, offsets, sorted_rows, w13_codes, w13_scales, b13, k: int = 4,
         _dev(h, "h", _BF16, (T * k, I))
     _check(_native.lib().moe_gate_up(
         _ptr(x), _ptr(offsets), _ptr(sorted_rows), _ptr(w13_codes), _ptr(w13_scales), _ptr(b13),
-        T, E, k, _ptr(h), _stream(x)), "moe_gate_up")
+        T, E, k, _ptr(h), _stream(x, offsets, sorted_rows, w13_codes, w13_scales, b13, h)),
+        "moe_gate_up")
     return h
 
 
@@ -205,7 +214,8 @@ def gate_up_mx6(x_records, offsets, sorted_rows, w13_codes, w13_scales, b13, k: 
         _dev(h, "h", _BF16, (T * k, I))
     _check(_native.lib().moe_gate_up_mx6(
         _ptr(x_records), _ptr(offsets), _ptr(sorted_rows), _ptr(w13_codes), _ptr(w13_scales),
-        _ptr(b13), T, E, k, _ptr(h), _stream(x_records)), "moe_gate_up_mx6")
+        _ptr(b13), T, E, k, _ptr(h),
+        _stream(x_records, offsets, sorted_rows, w13_codes, w13_scales, b13, h)), "moe_gate_up_mx6")
     return h
 
 
@@ -216,7 +226,7 @@ def down_accumulate(h, offsets, sorted_rows, topk_w, w2_codes, w2_scales, b2,
     E = w2_codes.shape[0]
     _dev(out, "out", _F32, (T, H))
     _dev(h, "h", _BF16, (T * k, I))
-    _dev(topk_w, "topk_w", _F32)
+    _dev(topk_w, "topk_w", _F32, (T, k))
     _dev(w2_codes, "w2_codes", _U8, (E, H, I // 2))
     _dev(w2_scales, "w2_scales", _U8, (E, H, I // 32))
     _dev(b2, "b2", _BF16, (E, H))
@@ -224,7 +234,8 @@ def down_accumulate(h, offsets, sorted_rows, topk_w, w2_codes, w2_scales, b2,
     _dev(sorted_rows, "sorted_rows", _I32, (T * k,))
     _check(_native.lib().moe_down_accumulate(
         _ptr(h), _ptr(offsets), _ptr(sorted_rows), _ptr(topk_w), _ptr(w2_codes), _ptr(w2_scales),
-        _ptr(b2), T, E, k, _ptr(out), _stream(out)), "moe_down_accumulate")
+        _ptr(b2), T, E, k, _ptr(out),
+        _stream(out, h, offsets, sorted_rows, topk_w, w2_codes, w2_scales, b2)), "moe_down_accumulate")
     return out
 
 
@@ -234,7 +245,7 @@ def combine(y: torch.Tensor, topk_w: torch.Tensor) -> torch.Tensor:
     _dev(y, "y", _F32, (T * k, H))
     _dev(topk_w, "topk_w", _F32)
     out = torch.empty((T, H), dtype=torch.float32, device=y.device)
-    _check(_native.lib().moe_combine(_ptr(y), _ptr(topk_w), T, k, _ptr(out), _stream(y)),
+    _check(_native.lib().moe_combine(_ptr(y), _ptr(topk_w), T, k, _ptr(out), _stream(y, topk_w)),
            "moe_combine")
     return out
 
@@ -271,7 +282,8 @@ def rmsnorm(x: torch.Tensor, scale: torch.Tensor, eps: float = 1e-5) -> torch.Te
     _dev(x, "x", _BF16, (T, H))
     _dev(scale, "scale", _F32, (H,))
     t = torch.empty((T, H), dtype=torch.int16, device=x.device)
-    _check(_native.lib().moe_rmsnorm(_ptr(x), _ptr(scale), float(eps), T, _ptr(t), _stream(x)),
+    _check(_native.lib().moe_rmsnorm(_ptr(x), _ptr(scale), float(eps), T, _ptr(t),
+                                     _stream(x, scale)),
            "moe_rmsnorm")
     return t
 
@@ -297,7 +309,9 @@ def forward_block(x, norm_scale, Wr, br, w13_codes, w13_scales, b13, w2_codes, w
     _check(_native.lib().moe_forward_block(
         _ptr(x), _ptr(norm_scale), float(norm_eps), _ptr(Wr), _ptr(br), _ptr(w13_codes),
         _ptr(w13_scales), _ptr(b13), _ptr(w2_codes), _ptr(w2_scales), _ptr(b2), T, E, k,
-        _ptr(out), _ptr(ws), ws.numel(), _stream(x)), "moe_forward_block")
+        _ptr(out), _ptr(ws), ws.numel(),
+        _stream(x, norm_scale, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, out, ws)),
+        "moe_forward_block")
     return out
 
 
@@ -318,5 +332,5 @@ def _forward(fn, x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
     _check(getattr(_native.lib(), fn)(
         _ptr(x), _ptr(Wr), _ptr(br), _ptr(w13_codes), _ptr(w13_scales), _ptr(b13),
         _ptr(w2_codes), _ptr(w2_scales), _ptr(b2), T, E, k, _ptr(out), _ptr(ws), ws.numel(),
-        _stream(x)), fn)
+        _stream(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, out, ws)), fn)
     return out
