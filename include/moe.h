@@ -158,6 +158,8 @@ moe_status_t moe_expert_ffn(const uint16_t* x, const int32_t* offsets,
  * moe_down_accumulate: down projection of h, weighted by the routing weight
  * and ADDED into out:
  *   out[t, :] += topk_w[s] * ( W2[e] h[p, :] + b2[e] ),  s = sorted_rows[p], t = s / k
+ *   h [T*k, 2880] bf16 as moe_gate_up wrote it; topk_w [T, k] fp32, indexed
+ *   by slot s = t*k + j (moe_route's weights).
  *   out [T, 2880] fp32 is accumulated, not overwritten: pass zeros for the
  *   layer output, or the residual stream to fold the residual add in. The
  *   order in which a token's k contributions are added is not fixed (atomic
