@@ -43,8 +43,12 @@
  *   weight tensor by moe_pack_weights (the "MXFP4 tensor packing" step named
  *   in the techniques map's inference list; the order itself is this
  *   library's). Packing permutes bytes inside each group of 64 rows only, so
- *   the packed arrays have exactly the canonical sizes. Every w13_codes,
- *   w13_scales, w2_codes, w2_scales argument below is packed.
+ *   the packed arrays have the canonical sizes. The GEMM entry points take a
+ *   packed tensor only through a moe_packed_weight_t descriptor that
+ *   moe_pack_weights has filled: raw code or scale pointers, in either
+ *   layout, cannot be passed to them, and a descriptor whose tag, expert
+ *   count or row count does not match the call is refused
+ *   (MOE_ERROR_LAYOUT).
  * - w13 rows are interleaved: row 2i is gate unit i, row 2i + 1 is up unit i.
  * - Alignment: x, Wr, out, y, h and every code array must be 16-byte aligned,
  *   the bias arrays b13 / b2 8-byte aligned and every scale array 4-byte
@@ -56,8 +60,10 @@
  * - Arguments are validated on the host before anything is launched; a
  *   failed launch returns MOE_ERROR_HIP. Device faults surface at the
  *   caller's next synchronisation. NaN/Inf inputs give undefined results.
- * - `ws` is caller-owned device scratch of at least moe_workspace_size(T,E,k)
- *   bytes, 256-byte aligned. Its contents on entry do not matter.
+ * - `ws` is caller-owned device scratch, 256-byte aligned, of at least
+ *   moe_workspace_size_op(op, T, E, k) bytes for the entry point's op
+ *   (moe_workspace_size(T, E, k) is enough for every op). Its contents on
+ *   entry do not matter.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -81,18 +87,55 @@ typedef enum moe_status {
   MOE_ERROR_MISALIGNED = 2,    /* a pointer lacks the alignment stated above  */
   MOE_ERROR_WORKSPACE = 3,     /* ws is NULL or smaller than required         */
   MOE_ERROR_UNSUPPORTED = 4,   /* current device is not gfx950                */
-  MOE_ERROR_HIP = 5            /* a HIP runtime call or launch failed         */
+  MOE_ERROR_HIP = 5,           /* a HIP runtime call or launch failed         */
+  MOE_ERROR_LAYOUT = 6         /* a weight descriptor not filled by           */
+                               /* moe_pack_weights, or of other E / N         */
 } moe_status_t;
 
-/* Bytes of scratch `ws` that every entry point below may use for (T, E, k).
- * Returns 0 when the sizes are out of range. */
+/* One packed MXFP4 weight tensor [E, N, K = 2880] (E experts of N rows).
+ * moe_pack_weights fills it; the library reads it on the host at call time
+ * only (the descriptor itself may live anywhere; codes and scales are device
+ * memory owned by the caller and must stay valid while kernels run). */
+#define MOE_PACKED_TAG 0x3450584Du /* "MXP4" */
+typedef struct moe_packed_weight {
+  const uint8_t* codes;   /* packed codes, E * N * 1440 bytes, 16-byte aligned */
+  const uint8_t* scales;  /* packed scales, E * N * 90 bytes, 4-byte aligned   */
+  int32_t E;              /* experts                                           */
+  int32_t N;              /* rows per expert: 5760 (gate/up) or 2880 (down)    */
+  uint32_t tag;           /* MOE_PACKED_TAG once packed                        */
+  uint32_t reserved;      /* 0                                                 */
+} moe_packed_weight_t;
+
+/* The entry points that take a workspace, for moe_workspace_size_op. */
+typedef enum moe_op {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_PERMUTE = 1,
+  MOE_OP_EXPERT_FFN = 2,
+  MOE_OP_FORWARD = 3,
+  MOE_OP_FORWARD_MX6 = 4,
+  MOE_OP_FORWARD_BLOCK = 5
+} moe_op_t;
+
+/* Bytes of scratch `ws` that the entry point `op` needs for (T, E, k): the
+ * routing arrays, the router's scratch and, for the layer calls, the
+ * intermediate h [T*k, 2880] bf16 and per-slot outputs [T*k, 2880] fp32
+ * (plus the FP6 records of moe_forward_mx6 and the normed input of
+ * moe_forward_block). At least 256. Returns 0 when the sizes or op are out
+ * of range. */
+size_t moe_workspace_size_op(moe_op_t op, int T, int E, int k);
+
+/* The largest moe_workspace_size_op over every op: one workspace of this size
+ * serves any call with these sizes. Returns 0 when the sizes are out of
+ * range. */
 size_t moe_workspace_size(int T, int E, int k);
 
 /* Packs one MXFP4 weight tensor from the canonical layout into the order the
- * expert GEMMs read (see the conventions above). N % 64 == 0, 64 <= N <= 65536,
- * 1 <= E <= 256; K = 2880.
+ * expert GEMMs read (see the conventions above) and fills `desc` (host
+ * memory) with the packed arrays, E, N and MOE_PACKED_TAG. N % 64 == 0,
+ * 64 <= N <= 65536, 1 <= E <= 256; K = 2880.
  *   codes [E, N, 1440] u8, scales [E, N, 90] u8 (canonical, in)
  *   packed_codes, packed_scales: same sizes (out; must not overlap the input)
+ *   desc: written only when the call succeeds
  * Packed order, per group G of rows [64G, 64G + 64) of one expert:
  *   codes: 23 K steps s of four MX blocks (4s .. 4s + 3); step s holds four
  *     16-row tiles m; tile m holds 64 lanes l = 16g + r of 16 bytes, lane l
@@ -102,7 +145,7 @@ size_t moe_workspace_size(int T, int E, int k);
  *   scales: offset = G*5760 + s*256 + l*4 + m for the same (s, m, l). */
 moe_status_t moe_pack_weights(const uint8_t* codes, const uint8_t* scales, int E, int N,
                               uint8_t* packed_codes, uint8_t* packed_scales,
-                              void* stream);
+                              moe_packed_weight_t* desc, void* stream);
 
 /* Router: logits = x Wr^T + br in fp32, then per token the k largest logits
  * (descending; equal logits -> lower expert id) and their softmax.
@@ -131,19 +174,16 @@ moe_status_t moe_permute(const int32_t* topk_ids, int T, int E, int k,
 /* Every routed slot through its expert, unweighted:
  *   y[t*k + j, :] = W2[e] h + b2[e],  h = SwiGLU(W13[e] x[t] + b13[e]), e = ids[t, j]
  *   offsets, sorted_rows   as produced by moe_permute
- *   w13_codes [E, 5760, 1440] u8   w13_scales [E, 5760, 90] u8   b13 [E, 5760] bf16
- *   w2_codes  [E, 2880, 1440] u8   w2_scales  [E, 2880, 90] u8   b2  [E, 2880] bf16
- *   (codes and scales packed by moe_pack_weights)
+ *   w13 packed gate/up weights (E experts x 5760 rows)    b13 [E, 5760] bf16
+ *   w2  packed down weights    (E experts x 2880 rows)    b2  [E, 2880] bf16
  *   y [T*k, 2880] fp32 (out)
  * The gate/up intermediate h is rounded to bf16 (the matrix-core input type).
  * Source: techniques map row "SwiGLU feed-forward"; swiglu_limit from the raw
  * config.json tables; MXFP4 from the "inference & serving" list. */
 moe_status_t moe_expert_ffn(const uint16_t* x, const int32_t* offsets,
                             const int32_t* sorted_rows,
-                            const uint8_t* w13_codes, const uint8_t* w13_scales,
-                            const uint16_t* b13,
-                            const uint8_t* w2_codes, const uint8_t* w2_scales,
-                            const uint16_t* b2,
+                            const moe_packed_weight_t* w13, const uint16_t* b13,
+                            const moe_packed_weight_t* w2, const uint16_t* b2,
                             int T, int E, int k, float* y,
                             void* ws, size_t ws_bytes, void* stream);
 
@@ -167,14 +207,14 @@ moe_status_t moe_expert_ffn(const uint16_t* x, const int32_t* offsets,
  *   Source: techniques map, "Mixture of experts" (weighted sum of experts). */
 moe_status_t moe_gate_up(const uint16_t* x, const int32_t* offsets,
                          const int32_t* sorted_rows,
-                         const uint8_t* w13_codes, const uint8_t* w13_scales,
-                         const uint16_t* b13, int T, int E, int k,
+                         const moe_packed_weight_t* w13, const uint16_t* b13,
+                         int T, int E, int k,
                          uint16_t* h, void* stream);
 
 moe_status_t moe_down_accumulate(const uint16_t* h, const int32_t* offsets,
                                  const int32_t* sorted_rows, const float* topk_w,
-                                 const uint8_t* w2_codes, const uint8_t* w2_scales,
-                                 const uint16_t* b2, int T, int E, int k,
+                                 const moe_packed_weight_t* w2, const uint16_t* b2,
+                                 int T, int E, int k,
                                  float* out, void* stream);
 
 /* out[t, :] = sum_j topk_w[t, j] * y[t*k + j, :]
@@ -192,10 +232,8 @@ moe_status_t moe_combine(const float* y, const float* topk_w, int T, int k,
  * ids instead of building the permutation.
  * Arguments as above; out [T, 2880] fp32 is overwritten. */
 moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
-                         const uint8_t* w13_codes, const uint8_t* w13_scales,
-                         const uint16_t* b13,
-                         const uint8_t* w2_codes, const uint8_t* w2_scales,
-                         const uint16_t* b2,
+                         const moe_packed_weight_t* w13, const uint16_t* b13,
+                         const moe_packed_weight_t* w2, const uint16_t* b2,
                          int T, int E, int k, float* out,
                          void* ws, size_t ws_bytes, void* stream);
 
@@ -217,10 +255,8 @@ moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
  * the piece encoding follows the OCP Microscaling v1.0 conversion and is
  * this library's. */
 moe_status_t moe_forward_mx6(const uint16_t* x, const float* Wr, const float* br,
-                             const uint8_t* w13_codes, const uint8_t* w13_scales,
-                             const uint16_t* b13,
-                             const uint8_t* w2_codes, const uint8_t* w2_scales,
-                             const uint16_t* b2,
+                             const moe_packed_weight_t* w13, const uint16_t* b13,
+                             const moe_packed_weight_t* w2, const uint16_t* b2,
                              int T, int E, int k, float* out,
                              void* ws, size_t ws_bytes, void* stream);
 
@@ -251,8 +287,8 @@ moe_status_t moe_encode_mx6(const uint16_t* x, int rows, uint8_t* records, void*
  * schedule. Other arguments, output and errors as moe_gate_up. */
 moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
                              const int32_t* sorted_rows,
-                             const uint8_t* w13_codes, const uint8_t* w13_scales,
-                             const uint16_t* b13, int T, int E, int k,
+                             const moe_packed_weight_t* w13, const uint16_t* b13,
+                             int T, int E, int k,
                              uint16_t* h, void* stream);
 
 /* The MoE sublayer of a gpt-oss decoder layer with its neighbours: the
@@ -270,10 +306,8 @@ moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
  * type); the residual is added in fp32. */
 moe_status_t moe_forward_block(const uint16_t* x, const float* norm_scale, float norm_eps,
                                const float* Wr, const float* br,
-                               const uint8_t* w13_codes, const uint8_t* w13_scales,
-                               const uint16_t* b13,
-                               const uint8_t* w2_codes, const uint8_t* w2_scales,
-                               const uint16_t* b2,
+                               const moe_packed_weight_t* w13, const uint16_t* b13,
+                               const moe_packed_weight_t* w2, const uint16_t* b2,
                                int T, int E, int k, float* out,
                                void* ws, size_t ws_bytes, void* stream);
 

@@ -5,12 +5,19 @@ stream into the C entry point of the same name in include/moe.h. Every step of
 the layer runs in the library's gfx950 kernels; this module only allocates
 outputs and workspace with torch and checks tensor properties.
 
+The expert weights enter the layer calls only as a PackedExperts (from
+pack_experts), whose packed MXFP4 tensors have shapes of their own
+([E, N/64, 92160] codes, [E, N/64, 5760] scales) and carry the descriptor the
+library's pack call filled; checkpoint-layout code and scale tensors are
+refused.
+
 bf16 tensors may be passed as torch.bfloat16 or as 16-bit integer tensors
 holding bf16 bit patterns.
 """
 from __future__ import annotations
 
 import ctypes
+from dataclasses import dataclass, field
 from typing import Optional
 
 import torch
@@ -20,11 +27,14 @@ from . import _native
 H = 2880
 I = 2880
 
-__all__ = ["MoeError", "workspace_size", "pack_weights", "pack_expert_weights", "route", "permute", "expert_ffn", "gate_up",
-           "down_accumulate", "combine", "forward", "forward_mx6", "encode_mx6", "gate_up_mx6", "forward_block", "rmsnorm",
-           "MX6_ROW_BYTES", "H", "I"]
+__all__ = ["MoeError", "PackedWeight", "PackedExperts", "workspace_size", "pack_weights",
+           "pack_experts", "route", "permute", "expert_ffn", "gate_up", "down_accumulate",
+           "combine", "forward", "forward_mx6", "encode_mx6", "gate_up_mx6", "forward_block",
+           "rmsnorm", "MX6_ROW_BYTES", "H", "I"]
 
 MX6_ROW_BYTES = 5888   # two-piece MX FP6 record bytes per activation row
+_GROUP_CODE_BYTES = 64 * (H // 2)    # packed codes of one 64-row group
+_GROUP_SCALE_BYTES = 64 * (H // 32)  # packed scales of one 64-row group
 
 
 class MoeError(RuntimeError):
@@ -73,15 +83,71 @@ def _stream(*ts: Optional[torch.Tensor]):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def workspace_size(T: int, E: int, k: int) -> int:
-    n = _native.lib().moe_workspace_size(T, E, k)
+@dataclass(eq=False)
+class PackedWeight:
+    """One MXFP4 weight tensor [E, N, 2880] in the library's packed order:
+    codes uint8 [E, N/64, 92160], scales uint8 [E, N/64, 5760], and the
+    moe_packed_weight_t descriptor the pack call filled. Made by pack_weights."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    E: int
+    N: int
+    _desc: _native.PackedWeightDesc = field(repr=False)
+
+    def desc(self):
+        """The C descriptor, checked to still describe these tensors."""
+        d = self._desc
+        if (d.tag != _native.MOE_PACKED_TAG or d.codes != self.codes.data_ptr()
+                or d.scales != self.scales.data_ptr() or d.E != self.E or d.N != self.N):
+            raise ValueError("packed weight descriptor no longer matches its tensors")
+        return ctypes.byref(d)
+
+
+@dataclass(eq=False)
+class PackedExperts:
+    """The expert weights of one layer as the expert GEMMs take them:
+    w13 (gate/up, N = 5760, rows interleaved gate/up) and w2 (down, N = 2880)
+    packed, and their bf16 biases b13 [E, 5760], b2 [E, 2880]."""
+    w13: PackedWeight
+    b13: torch.Tensor
+    w2: PackedWeight
+    b2: torch.Tensor
+
+    @property
+    def E(self) -> int:
+        return self.w13.E
+
+    def tensors(self):
+        return (self.w13.codes, self.w13.scales, self.b13, self.w2.codes, self.w2.scales, self.b2)
+
+
+def _experts(experts, E: Optional[int] = None) -> PackedExperts:
+    if not isinstance(experts, PackedExperts):
+        raise TypeError("expert weights must be a PackedExperts (from pack_experts); "
+                        "raw code / scale tensors are not accepted")
+    if experts.w13.N != 2 * I or experts.w2.N != H or experts.w2.E != experts.w13.E:
+        raise ValueError("PackedExperts: w13 must have 5760 rows, w2 2880, and the same experts")
+    _dev(experts.b13, "b13", _BF16, (experts.E, 2 * I))
+    _dev(experts.b2, "b2", _BF16, (experts.E, H))
+    if E is not None and experts.E != E:
+        raise ValueError(f"router has {E} experts, the expert weights {experts.E}")
+    return experts
+
+
+def workspace_size(T: int, E: int, k: int, op: Optional[str] = None) -> int:
+    """Workspace bytes of entry point `op` ('route', 'permute', 'expert_ffn',
+    'forward', 'forward_mx6', 'forward_block'); None: enough for any."""
+    if op is None:
+        n = _native.lib().moe_workspace_size(T, E, k)
+    else:
+        n = _native.lib().moe_workspace_size_op(_native.OPS[op], T, E, k)
     if n == 0:
         raise ValueError(f"sizes out of range: T={T} E={E} k={k}")
     return n
 
 
-def _workspace(T: int, E: int, k: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
-    need = workspace_size(T, E, k)
+def _workspace(T: int, E: int, k: int, device, ws: Optional[torch.Tensor], op: str) -> torch.Tensor:
+    need = workspace_size(T, E, k, op)
     if ws is None:
         return torch.empty(need, dtype=torch.uint8, device=device)
     _dev(ws, "workspace", _U8)
@@ -90,32 +156,32 @@ def _workspace(T: int, E: int, k: int, device, ws: Optional[torch.Tensor]) -> to
     return ws
 
 
-def _weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2):
-    E = w13_codes.shape[0]
-    _dev(w13_codes, "w13_codes", _U8, (E, 2 * I, H // 2))
-    _dev(w13_scales, "w13_scales", _U8, (E, 2 * I, H // 32))
-    _dev(b13, "b13", _BF16, (E, 2 * I))
-    _dev(w2_codes, "w2_codes", _U8, (E, H, I // 2))
-    _dev(w2_scales, "w2_scales", _U8, (E, H, I // 32))
-    _dev(b2, "b2", _BF16, (E, H))
-    return E
-
-
-def pack_weights(codes: torch.Tensor, scales: torch.Tensor):
-    """Canonical MXFP4 codes [E,N,1440] / scales [E,N,90] -> packed copies (same shapes)."""
+def pack_weights(codes: torch.Tensor, scales: torch.Tensor) -> PackedWeight:
+    """Canonical MXFP4 codes [E,N,1440] / scales [E,N,90] -> PackedWeight."""
     E, N = codes.shape[0], codes.shape[1]
     _dev(codes, "codes", _U8, (E, N, H // 2))
     _dev(scales, "scales", _U8, (E, N, H // 32))
-    pc = torch.empty_like(codes)
-    ps = torch.empty_like(scales)
+    if N % 64:
+        raise ValueError(f"rows per expert must be a multiple of 64, got {N}")
+    pc = torch.empty((E, N // 64, _GROUP_CODE_BYTES), dtype=torch.uint8, device=codes.device)
+    ps = torch.empty((E, N // 64, _GROUP_SCALE_BYTES), dtype=torch.uint8, device=codes.device)
+    d = _native.PackedWeightDesc()
     _check(_native.lib().moe_pack_weights(_ptr(codes), _ptr(scales), E, N, _ptr(pc), _ptr(ps),
-                                          _stream(codes, scales)), "moe_pack_weights")
-    return pc, ps
+                                          ctypes.byref(d), _stream(codes, scales)),
+           "moe_pack_weights")
+    return PackedWeight(pc, ps, E, N, d)
 
 
-def pack_expert_weights(w13_codes, w13_scales, w2_codes, w2_scales):
-    """Both expert weight tensors -> (w13_codes, w13_scales, w2_codes, w2_scales) packed."""
-    return (*pack_weights(w13_codes, w13_scales), *pack_weights(w2_codes, w2_scales))
+def pack_experts(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2) -> PackedExperts:
+    """Checkpoint-layout expert weights -> PackedExperts (one-time packing)."""
+    E = w13_codes.shape[0]
+    _dev(b13, "b13", _BF16, (E, 2 * I))
+    _dev(b2, "b2", _BF16, (E, H))
+    w13 = pack_weights(w13_codes, w13_scales)
+    w2 = pack_weights(w2_codes, w2_scales)
+    if w13.N != 2 * I or w2.N != H or w2.E != E:
+        raise ValueError("w13 must be [E, 5760, ...] and w2 [E, 2880, ...]")
+    return PackedExperts(w13, b13, w2, b2)
 
 
 def route(x: torch.Tensor, Wr: torch.Tensor, br: torch.Tensor, k: int = 4,
@@ -134,7 +200,7 @@ def route(x: torch.Tensor, Wr: torch.Tensor, br: torch.Tensor, k: int = 4,
     _dev(ids, "ids", _I32, (T, k))
     _dev(w, "w", _F32, (T, k))
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if return_logits else None
-    ws = _workspace(T, E, k, x.device, workspace)
+    ws = _workspace(T, E, k, x.device, workspace, "route")
     _check(_native.lib().moe_route(_ptr(x), _ptr(Wr), _ptr(br), T, E, k, _ptr(ids), _ptr(w),
                                    _ptr(logits), _ptr(ws), ws.numel(),
                                    _stream(x, Wr, br, ids, w, ws)), "moe_route")
@@ -149,41 +215,39 @@ def permute(topk_ids: torch.Tensor, E: int, workspace: Optional[torch.Tensor] = 
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     rows = torch.empty(T * k, dtype=torch.int32, device=dev)
-    ws = _workspace(T, E, k, dev, workspace)
+    ws = _workspace(T, E, k, dev, workspace, "permute")
     _check(_native.lib().moe_permute(_ptr(topk_ids), T, E, k, _ptr(counts), _ptr(offsets),
                                      _ptr(rows), _ptr(ws), ws.numel(), _stream(topk_ids, ws)),
            "moe_permute")
     return counts, offsets, rows
 
 
-def expert_ffn(x, offsets, sorted_rows, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
-               k: int = 4, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+def expert_ffn(x, offsets, sorted_rows, experts: PackedExperts, k: int = 4,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """-> y fp32 [T*k, 2880], unweighted expert output of every routed slot."""
     T = x.shape[0]
     _dev(x, "x", _BF16, (T, H))
-    E = _weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2)
+    ex = _experts(experts)
+    E = ex.E
     _dev(offsets, "offsets", _I32, (E + 1,))
     _dev(sorted_rows, "sorted_rows", _I32, (T * k,))
     y = torch.empty((T * k, H), dtype=torch.float32, device=x.device)
-    ws = _workspace(T, E, k, x.device, workspace)
+    ws = _workspace(T, E, k, x.device, workspace, "expert_ffn")
     _check(_native.lib().moe_expert_ffn(
-        _ptr(x), _ptr(offsets), _ptr(sorted_rows), _ptr(w13_codes), _ptr(w13_scales), _ptr(b13),
-        _ptr(w2_codes), _ptr(w2_scales), _ptr(b2), T, E, k, _ptr(y), _ptr(ws), ws.numel(),
-        _stream(x, offsets, sorted_rows, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, ws)),
-        "moe_expert_ffn")
+        _ptr(x), _ptr(offsets), _ptr(sorted_rows), ex.w13.desc(), _ptr(ex.b13), ex.w2.desc(),
+        _ptr(ex.b2), T, E, k, _ptr(y), _ptr(ws), ws.numel(),
+        _stream(x, offsets, sorted_rows, *ex.tensors(), ws)), "moe_expert_ffn")
     return y
 
 
-def gate_up(x, offsets, sorted_rows, w13_codes, w13_scales, b13, k: int = 4,
+def gate_up(x, offsets, sorted_rows, experts: PackedExperts, k: int = 4,
             h: Optional[torch.Tensor] = None) -> torch.Tensor:
     """-> h bf16 [T*k, 2880] (as int16 bits), SwiGLU of the gate/up projection
     of every routed slot, in expert-sorted order."""
     T = x.shape[0]
-    E = w13_codes.shape[0]
+    ex = _experts(experts)
+    E = ex.E
     _dev(x, "x", _BF16, (T, H))
-    _dev(w13_codes, "w13_codes", _U8, (E, 2 * I, H // 2))
-    _dev(w13_scales, "w13_scales", _U8, (E, 2 * I, H // 32))
-    _dev(b13, "b13", _BF16, (E, 2 * I))
     _dev(offsets, "offsets", _I32, (E + 1,))
     _dev(sorted_rows, "sorted_rows", _I32, (T * k,))
     if h is None:
@@ -191,21 +255,18 @@ def gate_up(x, offsets, sorted_rows, w13_codes, w13_scales, b13, k: int = 4,
     else:
         _dev(h, "h", _BF16, (T * k, I))
     _check(_native.lib().moe_gate_up(
-        _ptr(x), _ptr(offsets), _ptr(sorted_rows), _ptr(w13_codes), _ptr(w13_scales), _ptr(b13),
-        T, E, k, _ptr(h), _stream(x, offsets, sorted_rows, w13_codes, w13_scales, b13, h)),
-        "moe_gate_up")
+        _ptr(x), _ptr(offsets), _ptr(sorted_rows), ex.w13.desc(), _ptr(ex.b13), T, E, k, _ptr(h),
+        _stream(x, offsets, sorted_rows, ex.w13.codes, ex.w13.scales, ex.b13, h)), "moe_gate_up")
     return h
 
 
-def gate_up_mx6(x_records, offsets, sorted_rows, w13_codes, w13_scales, b13, k: int = 4,
+def gate_up_mx6(x_records, offsets, sorted_rows, experts: PackedExperts, k: int = 4,
                 h: Optional[torch.Tensor] = None) -> torch.Tensor:
     """gate_up with the activations as encode_mx6 records uint8 [T, 23, 256]."""
     T = x_records.shape[0]
-    E = w13_codes.shape[0]
+    ex = _experts(experts)
+    E = ex.E
     _dev(x_records, "x_records", _U8, (T, 23, 256))
-    _dev(w13_codes, "w13_codes", _U8, (E, 2 * I, H // 2))
-    _dev(w13_scales, "w13_scales", _U8, (E, 2 * I, H // 32))
-    _dev(b13, "b13", _BF16, (E, 2 * I))
     _dev(offsets, "offsets", _I32, (E + 1,))
     _dev(sorted_rows, "sorted_rows", _I32, (T * k,))
     if h is None:
@@ -213,29 +274,27 @@ def gate_up_mx6(x_records, offsets, sorted_rows, w13_codes, w13_scales, b13, k: 
     else:
         _dev(h, "h", _BF16, (T * k, I))
     _check(_native.lib().moe_gate_up_mx6(
-        _ptr(x_records), _ptr(offsets), _ptr(sorted_rows), _ptr(w13_codes), _ptr(w13_scales),
-        _ptr(b13), T, E, k, _ptr(h),
-        _stream(x_records, offsets, sorted_rows, w13_codes, w13_scales, b13, h)), "moe_gate_up_mx6")
+        _ptr(x_records), _ptr(offsets), _ptr(sorted_rows), ex.w13.desc(), _ptr(ex.b13), T, E, k,
+        _ptr(h), _stream(x_records, offsets, sorted_rows, ex.w13.codes, ex.w13.scales, ex.b13, h)),
+        "moe_gate_up_mx6")
     return h
 
 
-def down_accumulate(h, offsets, sorted_rows, topk_w, w2_codes, w2_scales, b2,
+def down_accumulate(h, offsets, sorted_rows, topk_w, experts: PackedExperts,
                     out: torch.Tensor, k: int = 4) -> torch.Tensor:
     """out[t] += sum_j topk_w[t, j] * (W2[e] h + b2[e]) over the slots of t; returns out."""
     T = out.shape[0]
-    E = w2_codes.shape[0]
+    ex = _experts(experts)
+    E = ex.E
     _dev(out, "out", _F32, (T, H))
     _dev(h, "h", _BF16, (T * k, I))
     _dev(topk_w, "topk_w", _F32, (T, k))
-    _dev(w2_codes, "w2_codes", _U8, (E, H, I // 2))
-    _dev(w2_scales, "w2_scales", _U8, (E, H, I // 32))
-    _dev(b2, "b2", _BF16, (E, H))
     _dev(offsets, "offsets", _I32, (E + 1,))
     _dev(sorted_rows, "sorted_rows", _I32, (T * k,))
     _check(_native.lib().moe_down_accumulate(
-        _ptr(h), _ptr(offsets), _ptr(sorted_rows), _ptr(topk_w), _ptr(w2_codes), _ptr(w2_scales),
-        _ptr(b2), T, E, k, _ptr(out),
-        _stream(out, h, offsets, sorted_rows, topk_w, w2_codes, w2_scales, b2)), "moe_down_accumulate")
+        _ptr(h), _ptr(offsets), _ptr(sorted_rows), _ptr(topk_w), ex.w2.desc(), _ptr(ex.b2), T, E, k,
+        _ptr(out), _stream(out, h, offsets, sorted_rows, topk_w, ex.w2.codes, ex.w2.scales, ex.b2)),
+        "moe_down_accumulate")
     return out
 
 
@@ -250,21 +309,18 @@ def combine(y: torch.Tensor, topk_w: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def forward(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, k: int = 4,
-            out: Optional[torch.Tensor] = None,
+def forward(x, Wr, br, experts: PackedExperts, k: int = 4, out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole layer -> out fp32 [T, 2880]."""
-    return _forward("moe_forward", x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales,
-                    b2, k, out, workspace)
+    return _forward("moe_forward", "forward", x, Wr, br, experts, k, out, workspace)
 
 
-def forward_mx6(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, k: int = 4,
+def forward_mx6(x, Wr, br, experts: PackedExperts, k: int = 4,
                 out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole layer with the tiled expert GEMMs on the block-scaled FP4 x FP6
     matrix cores (activations as two MX FP6 pieces) -> out fp32 [T, 2880]."""
-    return _forward("moe_forward_mx6", x, Wr, br, w13_codes, w13_scales, b13, w2_codes,
-                    w2_scales, b2, k, out, workspace)
+    return _forward("moe_forward_mx6", "forward_mx6", x, Wr, br, experts, k, out, workspace)
 
 
 def encode_mx6(x: torch.Tensor) -> torch.Tensor:
@@ -288,8 +344,8 @@ def rmsnorm(x: torch.Tensor, scale: torch.Tensor, eps: float = 1e-5) -> torch.Te
     return t
 
 
-def forward_block(x, norm_scale, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
-                  k: int = 4, norm_eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+def forward_block(x, norm_scale, Wr, br, experts: PackedExperts, k: int = 4,
+                  norm_eps: float = 1e-5, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out fp32 [T, 2880] = x + layer(bf16(RMSNorm(x))): the MoE sublayer of a
     decoder layer with its pre-norm and residual add."""
@@ -299,38 +355,32 @@ def forward_block(x, norm_scale, Wr, br, w13_codes, w13_scales, b13, w2_codes, w
     _dev(norm_scale, "norm_scale", _F32, (H,))
     _dev(Wr, "Wr", _F32, (E, H))
     _dev(br, "br", _F32, (E,))
-    if _weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2) != E:
-        raise ValueError("router and expert weights disagree on the expert count")
+    ex = _experts(experts, E)
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=x.device)
     else:
         _dev(out, "out", _F32, (T, H))
-    ws = _workspace(T, E, k, x.device, workspace)
+    ws = _workspace(T, E, k, x.device, workspace, "forward_block")
     _check(_native.lib().moe_forward_block(
-        _ptr(x), _ptr(norm_scale), float(norm_eps), _ptr(Wr), _ptr(br), _ptr(w13_codes),
-        _ptr(w13_scales), _ptr(b13), _ptr(w2_codes), _ptr(w2_scales), _ptr(b2), T, E, k,
-        _ptr(out), _ptr(ws), ws.numel(),
-        _stream(x, norm_scale, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, out, ws)),
-        "moe_forward_block")
+        _ptr(x), _ptr(norm_scale), float(norm_eps), _ptr(Wr), _ptr(br), ex.w13.desc(),
+        _ptr(ex.b13), ex.w2.desc(), _ptr(ex.b2), T, E, k, _ptr(out), _ptr(ws), ws.numel(),
+        _stream(x, norm_scale, Wr, br, *ex.tensors(), out, ws)), "moe_forward_block")
     return out
 
 
-def _forward(fn, x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, k, out,
-             workspace) -> torch.Tensor:
+def _forward(fn, op, x, Wr, br, experts, k, out, workspace) -> torch.Tensor:
     T = x.shape[0]
     E = Wr.shape[0]
     _dev(x, "x", _BF16, (T, H))
     _dev(Wr, "Wr", _F32, (E, H))
     _dev(br, "br", _F32, (E,))
-    if _weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2) != E:
-        raise ValueError("router and expert weights disagree on the expert count")
+    ex = _experts(experts, E)
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=x.device)
     else:
         _dev(out, "out", _F32, (T, H))
-    ws = _workspace(T, E, k, x.device, workspace)
+    ws = _workspace(T, E, k, x.device, workspace, op)
     _check(getattr(_native.lib(), fn)(
-        _ptr(x), _ptr(Wr), _ptr(br), _ptr(w13_codes), _ptr(w13_scales), _ptr(b13),
-        _ptr(w2_codes), _ptr(w2_scales), _ptr(b2), T, E, k, _ptr(out), _ptr(ws), ws.numel(),
-        _stream(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, out, ws)), fn)
+        _ptr(x), _ptr(Wr), _ptr(br), ex.w13.desc(), _ptr(ex.b13), ex.w2.desc(), _ptr(ex.b2),
+        T, E, k, _ptr(out), _ptr(ws), ws.numel(), _stream(x, Wr, br, *ex.tensors(), out, ws)), fn)
     return out

@@ -29,30 +29,44 @@ bool sizes_ok(int T, int E, int k) {
   return (long long)T * k <= MOE_MAX_ROUTED;
 }
 
-WsLayout layout(int T, int E, int k) {
+bool op_ok(int op) { return op >= MOE_OP_ROUTE && op <= MOE_OP_FORWARD_BLOCK; }
+
+// Carve-up of the workspace of entry point `op`: only what that call uses.
+// Regions an op does not use have size 0 (their offsets are then unused).
+WsLayout layout(moe_op_t op, int T, int E, int k) {
   const size_t n = (size_t)T * k;
+  const bool layer = op == MOE_OP_FORWARD || op == MOE_OP_FORWARD_MX6 || op == MOE_OP_FORWARD_BLOCK;
+  const bool tiles = n > 0 && moe::ffn_uses_tiles((int)n, E);
   WsLayout l;
   size_t off = 0;
-  l.ids = off;      off = align_up(off + n * 4);
-  l.w = off;        off = align_up(off + n * 4);
-  l.counts = off;   off = align_up(off + (size_t)E * 4);
-  l.offsets = off;  off = align_up(off + (size_t)(E + 1) * 4);
-  l.sorted = off;   off = align_up(off + n * 4);
-  l.scratch = off;  off = align_up(off + moe::route_scratch_bytes(T, E));
-  l.h = off;        off = align_up(off + n * (size_t)moe::kI * 2);
+  auto take = [&](size_t& at, size_t bytes) {
+    at = off;
+    off = align_up(off + bytes);
+  };
+  // routing results and the permutation (the layer calls)
+  take(l.ids, layer ? n * 4 : 0);
+  take(l.w, layer ? n * 4 : 0);
+  take(l.counts, layer ? (size_t)E * 4 : 0);
+  take(l.offsets, layer ? (size_t)(E + 1) * 4 : 0);
+  take(l.sorted, layer ? n * 4 : 0);
+  // router partial logits or per-block expert histograms; the standalone
+  // permutation's histograms (only above one workgroup's slots)
+  size_t scratch = 0;
+  if (op == MOE_OP_ROUTE || layer) scratch = moe::route_scratch_bytes(T, E);
+  if (op == MOE_OP_PERMUTE) scratch = n > 1024 ? (size_t)((T + 31) / 32) * E * 4 : 0;
+  take(l.scratch, scratch);
+  // the gate/up output h [T*k, 2880] bf16 in expert-sorted order
+  take(l.h, (layer || op == MOE_OP_EXPERT_FFN) ? n * (size_t)moe::kI * 2 : 0);
   // per-slot fp32 expert outputs: the layer stores them and sums a token's k
   // rows in a second pass instead of atomically adding into out
-  l.y = off;        off = align_up(off + n * (size_t)moe::kH * 4);
-  const bool tiles = n > 0 && moe::ffn_uses_tiles((int)n, E);
-  // the tiled schedule of moe_forward_mx6: x as two-piece MX FP6 records
-  l.xrec = off;
-  if (tiles) off = align_up(off + (size_t)T * moe::kRowRecBytes);
+  take(l.y, layer ? n * (size_t)moe::kH * 4 : 0);
+  // moe_forward_mx6, tiled schedule: x and h as two-piece MX FP6 records
+  const bool mx6 = op == MOE_OP_FORWARD_MX6 && tiles;
+  take(l.xrec, mx6 ? (size_t)T * moe::kRowRecBytes : 0);
+  take(l.hrec, mx6 ? n * (size_t)moe::kRowRecBytes : 0);
   // moe_forward_block: the normed bf16 input of the layer
-  l.xnorm = off;    off = align_up(off + (size_t)T * moe::kH * 2);
-  // moe_forward_mx6, tiled schedule: h as two-piece MX FP6 records
-  l.hrec = off;
-  if (tiles) off = align_up(off + n * (size_t)moe::kRowRecBytes);
-  l.total = off;
+  take(l.xnorm, op == MOE_OP_FORWARD_BLOCK ? (size_t)T * moe::kH * 2 : 0);
+  l.total = off < kAlign ? kAlign : off;
   return l;
 }
 
@@ -98,31 +112,41 @@ moe_status_t after_launch(hipError_t err, hipStream_t s) {
     if (st_ != MOE_SUCCESS) return st_;     \
   } while (0)
 
-moe_status_t check_weights(const uint8_t* w13c, const uint8_t* w13s, const uint16_t* b13,
-                           const uint8_t* w2c, const uint8_t* w2s, const uint16_t* b2) {
-  if (!w13c || !w13s || !b13 || !w2c || !w2s || !b2) return MOE_ERROR_INVALID_VALUE;
-  if (!aligned(w13c, 16) || !aligned(w2c, 16) || !aligned(w13s, 4) || !aligned(w2s, 4) ||
-      !aligned(b13, 8) || !aligned(b2, 8))
-    return MOE_ERROR_MISALIGNED;
+// A packed weight tensor: filled by moe_pack_weights, with the call's expert
+// count and rows per expert.
+moe_status_t check_packed(const moe_packed_weight_t* w, int E, int N) {
+  if (!w) return MOE_ERROR_INVALID_VALUE;
+  if (w->tag != MOE_PACKED_TAG || w->E != E || w->N != N) return MOE_ERROR_LAYOUT;
+  if (!w->codes || !w->scales) return MOE_ERROR_LAYOUT;
+  if (!aligned(w->codes, 16) || !aligned(w->scales, 4)) return MOE_ERROR_MISALIGNED;
   return MOE_SUCCESS;
 }
 
-moe_status_t check_ws(void* ws, size_t ws_bytes, int T, int E, int k) {
+moe_status_t check_weights(const moe_packed_weight_t* w13, const uint16_t* b13,
+                           const moe_packed_weight_t* w2, const uint16_t* b2, int E) {
+  if (!b13 || !b2) return MOE_ERROR_INVALID_VALUE;
+  MOE_TRY(check_packed(w13, E, moe::kN13));
+  MOE_TRY(check_packed(w2, E, moe::kH));
+  if (!aligned(b13, 8) || !aligned(b2, 8)) return MOE_ERROR_MISALIGNED;
+  return MOE_SUCCESS;
+}
+
+moe_status_t check_ws(void* ws, size_t ws_bytes, moe_op_t op, int T, int E, int k) {
   if (!ws || !aligned(ws, kAlign)) return MOE_ERROR_WORKSPACE;
-  if (ws_bytes < layout(T, E, k).total) return MOE_ERROR_WORKSPACE;
+  if (ws_bytes < layout(op, T, E, k).total) return MOE_ERROR_WORKSPACE;
   return MOE_SUCCESS;
 }
 
 FfnArgs ffn_args(const uint16_t* act, const int32_t* offsets, const int32_t* sorted_rows,
-                 const uint8_t* codes, const uint8_t* scales, const uint16_t* bias, int N, int E,
-                 int k, int gather) {
+                 const moe_packed_weight_t* w, const uint16_t* bias, int N, int E, int k,
+                 int gather) {
   FfnArgs a;
   std::memset(&a, 0, sizeof a);
   a.act = act;
   a.offsets = offsets;
   a.sorted_rows = sorted_rows;
-  a.codes = codes;
-  a.scales = scales;
+  a.codes = w->codes;
+  a.scales = w->scales;
   a.bias = bias;
   a.N = N;
   a.E = E;
@@ -135,9 +159,19 @@ FfnArgs ffn_args(const uint16_t* act, const int32_t* offsets, const int32_t* sor
 
 extern "C" {
 
+size_t moe_workspace_size_op(moe_op_t op, int T, int E, int k) {
+  if (!sizes_ok(T, E, k) || !op_ok(op)) return 0;
+  return layout(op, T, E, k).total;
+}
+
 size_t moe_workspace_size(int T, int E, int k) {
   if (!sizes_ok(T, E, k)) return 0;
-  return layout(T, E, k).total;
+  size_t m = 0;
+  for (int op = MOE_OP_ROUTE; op <= MOE_OP_FORWARD_BLOCK; ++op) {
+    const size_t b = layout(static_cast<moe_op_t>(op), T, E, k).total;
+    m = b > m ? b : m;
+  }
+  return m;
 }
 
 const char* moe_status_string(moe_status_t status) {
@@ -148,6 +182,8 @@ const char* moe_status_string(moe_status_t status) {
     case MOE_ERROR_WORKSPACE: return "MOE_ERROR_WORKSPACE: workspace missing, misaligned or too small";
     case MOE_ERROR_UNSUPPORTED: return "MOE_ERROR_UNSUPPORTED: current device is not gfx950";
     case MOE_ERROR_HIP: return "MOE_ERROR_HIP: a HIP runtime call or kernel launch failed";
+    case MOE_ERROR_LAYOUT:
+      return "MOE_ERROR_LAYOUT: weight descriptor not filled by moe_pack_weights or of other E / N";
   }
   return "unknown moe_status_t";
 }
@@ -161,24 +197,33 @@ moe_status_t moe_route(const uint16_t* x, const float* Wr, const float* br, int 
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(br, 4) || !aligned(topk_ids, 4) ||
       !aligned(topk_w, 4) || !aligned(logits, 4))
     return MOE_ERROR_MISALIGNED;
-  MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
+  MOE_TRY(check_ws(ws, ws_bytes, MOE_OP_ROUTE, T, E, k));
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* scratch = reinterpret_cast<float*>(static_cast<char*>(ws) + layout(T, E, k).scratch);
+  float* scratch =
+      reinterpret_cast<float*>(static_cast<char*>(ws) + layout(MOE_OP_ROUTE, T, E, k).scratch);
   return after_launch(moe::launch_route(x, Wr, br, T, E, k, topk_ids, topk_w, logits, scratch, nullptr,
                                         nullptr, nullptr, s), s);
 }
 
 moe_status_t moe_pack_weights(const uint8_t* codes, const uint8_t* scales, int E, int N,
-                              uint8_t* packed_codes, uint8_t* packed_scales, void* stream) {
+                              uint8_t* packed_codes, uint8_t* packed_scales,
+                              moe_packed_weight_t* desc, void* stream) {
   if (E < 1 || E > MOE_MAX_EXPERTS || N < 64 || N > 65536 || N % 64 != 0)
     return MOE_ERROR_INVALID_VALUE;
-  if (!codes || !scales || !packed_codes || !packed_scales) return MOE_ERROR_INVALID_VALUE;
+  if (!codes || !scales || !packed_codes || !packed_scales || !desc) return MOE_ERROR_INVALID_VALUE;
   if (!aligned(codes, 16) || !aligned(packed_codes, 16) || !aligned(packed_scales, 4))
     return MOE_ERROR_MISALIGNED;
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(moe::launch_pack(codes, scales, E, N, packed_codes, packed_scales, s), s);
+  MOE_TRY(after_launch(moe::launch_pack(codes, scales, E, N, packed_codes, packed_scales, s), s));
+  desc->codes = packed_codes;
+  desc->scales = packed_scales;
+  desc->E = E;
+  desc->N = N;
+  desc->tag = MOE_PACKED_TAG;
+  desc->reserved = 0;
+  return MOE_SUCCESS;
 }
 
 moe_status_t moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* counts,
@@ -189,70 +234,69 @@ moe_status_t moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* 
   if (!topk_ids || !counts || !offsets || !sorted_rows) return MOE_ERROR_INVALID_VALUE;
   if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_rows, 4))
     return MOE_ERROR_MISALIGNED;
-  MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
+  MOE_TRY(check_ws(ws, ws_bytes, MOE_OP_PERMUTE, T, E, k));
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + layout(T, E, k).scratch);
+  int32_t* hist =
+      reinterpret_cast<int32_t*>(static_cast<char*>(ws) + layout(MOE_OP_PERMUTE, T, E, k).scratch);
   return after_launch(moe::launch_permute(topk_ids, T * k, E, k, counts, offsets, sorted_rows, hist, s),
                       s);
 }
 
 moe_status_t moe_expert_ffn(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_rows,
-                            const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
-                            const uint8_t* w2_codes, const uint8_t* w2_scales, const uint16_t* b2,
-                            int T, int E, int k, float* y, void* ws, size_t ws_bytes, void* stream) {
+                            const moe_packed_weight_t* w13, const uint16_t* b13,
+                            const moe_packed_weight_t* w2, const uint16_t* b2, int T, int E, int k,
+                            float* y, void* ws, size_t ws_bytes, void* stream) {
   if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
   if (T == 0) return MOE_SUCCESS;
   if (!x || !offsets || !sorted_rows || !y) return MOE_ERROR_INVALID_VALUE;
-  MOE_TRY(check_weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2));
+  MOE_TRY(check_weights(w13, b13, w2, b2, E));
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(offsets, 4) || !aligned(sorted_rows, 4))
     return MOE_ERROR_MISALIGNED;
-  MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
+  MOE_TRY(check_ws(ws, ws_bytes, MOE_OP_EXPERT_FFN, T, E, k));
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const WsLayout l = layout(T, E, k);
+  const WsLayout l = layout(MOE_OP_EXPERT_FFN, T, E, k);
   uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + l.h);
   const int n = T * k;
-  FfnArgs a13 = ffn_args(x, offsets, sorted_rows, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
+  FfnArgs a13 = ffn_args(x, offsets, sorted_rows, w13, b13, moe::kN13, E, k, 1);
   a13.h_out = h;
   MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));
-  FfnArgs a2 = ffn_args(h, offsets, sorted_rows, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
+  FfnArgs a2 = ffn_args(h, offsets, sorted_rows, w2, b2, moe::kH, E, k, 0);
   a2.y_out = y;
   return after_launch(moe::launch_ffn(a2, moe::EPI_STORE_Y, n, s), s);
 }
 
 moe_status_t moe_gate_up(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_rows,
-                         const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
-                         int T, int E, int k, uint16_t* h, void* stream) {
+                         const moe_packed_weight_t* w13, const uint16_t* b13, int T, int E, int k,
+                         uint16_t* h, void* stream) {
   if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
   if (T == 0) return MOE_SUCCESS;
-  if (!x || !offsets || !sorted_rows || !w13_codes || !w13_scales || !b13 || !h)
-    return MOE_ERROR_INVALID_VALUE;
-  if (!aligned(x, 16) || !aligned(h, 16) || !aligned(w13_codes, 16) || !aligned(w13_scales, 4) ||
-      !aligned(b13, 8) || !aligned(offsets, 4) || !aligned(sorted_rows, 4))
+  if (!x || !offsets || !sorted_rows || !b13 || !h) return MOE_ERROR_INVALID_VALUE;
+  MOE_TRY(check_packed(w13, E, moe::kN13));
+  if (!aligned(x, 16) || !aligned(h, 16) || !aligned(b13, 8) || !aligned(offsets, 4) ||
+      !aligned(sorted_rows, 4))
     return MOE_ERROR_MISALIGNED;
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  FfnArgs a = ffn_args(x, offsets, sorted_rows, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
+  FfnArgs a = ffn_args(x, offsets, sorted_rows, w13, b13, moe::kN13, E, k, 1);
   a.h_out = h;
   return after_launch(moe::launch_ffn(a, moe::EPI_SWIGLU, T * k, s), s);
 }
 
 moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
-                             const int32_t* sorted_rows, const uint8_t* w13_codes,
-                             const uint8_t* w13_scales, const uint16_t* b13, int T, int E, int k,
-                             uint16_t* h, void* stream) {
+                             const int32_t* sorted_rows, const moe_packed_weight_t* w13,
+                             const uint16_t* b13, int T, int E, int k, uint16_t* h, void* stream) {
   if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
   if (T == 0) return MOE_SUCCESS;
-  if (!x_records || !offsets || !sorted_rows || !w13_codes || !w13_scales || !b13 || !h)
-    return MOE_ERROR_INVALID_VALUE;
-  if (!aligned(x_records, 16) || !aligned(h, 16) || !aligned(w13_codes, 16) ||
-      !aligned(w13_scales, 4) || !aligned(b13, 8) || !aligned(offsets, 4) ||
+  if (!x_records || !offsets || !sorted_rows || !b13 || !h) return MOE_ERROR_INVALID_VALUE;
+  MOE_TRY(check_packed(w13, E, moe::kN13));
+  if (!aligned(x_records, 16) || !aligned(h, 16) || !aligned(b13, 8) || !aligned(offsets, 4) ||
       !aligned(sorted_rows, 4))
     return MOE_ERROR_MISALIGNED;
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  FfnArgs a = ffn_args(nullptr, offsets, sorted_rows, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
+  FfnArgs a = ffn_args(nullptr, offsets, sorted_rows, w13, b13, moe::kN13, E, k, 1);
   a.act6 = x_records;
   a.h_out = h;
   return after_launch(moe::launch_ffn(a, moe::EPI_SWIGLU, T * k, s), s);
@@ -260,19 +304,18 @@ moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
 
 moe_status_t moe_down_accumulate(const uint16_t* h, const int32_t* offsets,
                                  const int32_t* sorted_rows, const float* topk_w,
-                                 const uint8_t* w2_codes, const uint8_t* w2_scales,
-                                 const uint16_t* b2, int T, int E, int k, float* out,
-                                 void* stream) {
+                                 const moe_packed_weight_t* w2, const uint16_t* b2, int T, int E,
+                                 int k, float* out, void* stream) {
   if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
   if (T == 0) return MOE_SUCCESS;
-  if (!h || !offsets || !sorted_rows || !topk_w || !w2_codes || !w2_scales || !b2 || !out)
-    return MOE_ERROR_INVALID_VALUE;
-  if (!aligned(h, 16) || !aligned(out, 16) || !aligned(w2_codes, 16) || !aligned(w2_scales, 4) ||
-      !aligned(b2, 8) || !aligned(offsets, 4) || !aligned(sorted_rows, 4) || !aligned(topk_w, 4))
+  if (!h || !offsets || !sorted_rows || !topk_w || !b2 || !out) return MOE_ERROR_INVALID_VALUE;
+  MOE_TRY(check_packed(w2, E, moe::kH));
+  if (!aligned(h, 16) || !aligned(out, 16) || !aligned(b2, 8) || !aligned(offsets, 4) ||
+      !aligned(sorted_rows, 4) || !aligned(topk_w, 4))
     return MOE_ERROR_MISALIGNED;
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  FfnArgs a = ffn_args(h, offsets, sorted_rows, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
+  FfnArgs a = ffn_args(h, offsets, sorted_rows, w2, b2, moe::kH, E, k, 0);
   a.topk_w = topk_w;
   a.out = out;
   return after_launch(moe::launch_ffn(a, moe::EPI_COMBINE, T * k, s), s);
@@ -294,38 +337,18 @@ moe_status_t moe_combine(const float* y, const float* topk_w, int T, int k, floa
 
 namespace {
 
+struct LayerWeights {
+  const moe_packed_weight_t* w13;
+  const uint16_t* b13;
+  const moe_packed_weight_t* w2;
+  const uint16_t* b2;
+};
+
 // The layer on x; with `resid` (bf16 [T, 2880]) the output is resid + layer.
-// Arguments are validated by the caller.
+// Arguments are validated by the caller; `l` is the caller's workspace layout.
 moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
-                            const uint8_t* w13_codes, const uint8_t* w13_scales,
-                            const uint16_t* b13, const uint8_t* w2_codes, const uint8_t* w2_scales,
-                            const uint16_t* b2, int T, int E, int k, float* out, void* ws,
-                            hipStream_t s, bool mx6, const uint16_t* resid);
-
-moe_status_t forward_impl(const uint16_t* x, const float* Wr, const float* br,
-                          const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
-                          const uint8_t* w2_codes, const uint8_t* w2_scales, const uint16_t* b2,
-                          int T, int E, int k, float* out, void* ws, size_t ws_bytes, void* stream,
-                          bool mx6) {
-  if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
-  if (T == 0) return MOE_SUCCESS;
-  if (!x || !Wr || !br || !out) return MOE_ERROR_INVALID_VALUE;
-  MOE_TRY(check_weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2));
-  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(out, 16) || !aligned(br, 4))
-    return MOE_ERROR_MISALIGNED;
-  MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
-  MOE_TRY(check_device());
-  return forward_launch(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, E, k,
-                        out, ws, static_cast<hipStream_t>(stream), mx6, nullptr);
-}
-
-moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
-                            const uint8_t* w13_codes, const uint8_t* w13_scales,
-                            const uint16_t* b13, const uint8_t* w2_codes, const uint8_t* w2_scales,
-                            const uint16_t* b2, int T, int E, int k, float* out, void* ws,
-                            hipStream_t s, bool mx6, const uint16_t* resid) {
-  const WsLayout l = layout(T, E, k);
-  char* base = static_cast<char*>(ws);
+                            const LayerWeights& lw, int T, int E, int k, float* out, char* base,
+                            const WsLayout& l, hipStream_t s, bool mx6, const uint16_t* resid) {
   int32_t* ids = reinterpret_cast<int32_t*>(base + l.ids);
   float* w = reinterpret_cast<float*>(base + l.w);
   int32_t* counts = reinterpret_cast<int32_t*>(base + l.counts);
@@ -340,7 +363,7 @@ moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
   // their slots in the routing ids.
   MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, scratch,
                                          tiles ? counts : nullptr, offsets, sorted, s), s));
-  FfnArgs a13 = ffn_args(x, offsets, sorted, w13_codes, w13_scales, b13, moe::kN13, E, k, 1);
+  FfnArgs a13 = ffn_args(x, offsets, sorted, lw.w13, lw.b13, moe::kN13, E, k, 1);
   a13.h_out = h;
   if (!tiles) {
     a13.ids = ids;
@@ -354,7 +377,7 @@ moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
     a13.h6_out = reinterpret_cast<uint8_t*>(base + l.hrec);
   }
   MOE_TRY(after_launch(moe::launch_ffn(a13, moe::EPI_SWIGLU, n, s), s));
-  FfnArgs a2 = ffn_args(h, offsets, sorted, w2_codes, w2_scales, b2, moe::kH, E, k, 0);
+  FfnArgs a2 = ffn_args(h, offsets, sorted, lw.w2, lw.b2, moe::kH, E, k, 0);
   if (!tiles) {
     a2.ids = ids;
     a2.n_slots = n;
@@ -370,25 +393,40 @@ moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
   return after_launch(moe::launch_combine(y, w, T, k, resid, out, s), s);
 }
 
+moe_status_t forward_impl(const uint16_t* x, const float* Wr, const float* br,
+                          const LayerWeights& lw, int T, int E, int k, float* out, void* ws,
+                          size_t ws_bytes, void* stream, bool mx6) {
+  if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !Wr || !br || !out) return MOE_ERROR_INVALID_VALUE;
+  MOE_TRY(check_weights(lw.w13, lw.b13, lw.w2, lw.b2, E));
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(out, 16) || !aligned(br, 4))
+    return MOE_ERROR_MISALIGNED;
+  const moe_op_t op = mx6 ? MOE_OP_FORWARD_MX6 : MOE_OP_FORWARD;
+  MOE_TRY(check_ws(ws, ws_bytes, op, T, E, k));
+  MOE_TRY(check_device());
+  return forward_launch(x, Wr, br, lw, T, E, k, out, static_cast<char*>(ws), layout(op, T, E, k),
+                        static_cast<hipStream_t>(stream), mx6, nullptr);
+}
+
 }  // namespace
 
 extern "C" {
 
 moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
-                         const uint8_t* w13_codes, const uint8_t* w13_scales, const uint16_t* b13,
-                         const uint8_t* w2_codes, const uint8_t* w2_scales, const uint16_t* b2,
-                         int T, int E, int k, float* out, void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, E, k, out,
-                      ws, ws_bytes, stream, false);
+                         const moe_packed_weight_t* w13, const uint16_t* b13,
+                         const moe_packed_weight_t* w2, const uint16_t* b2, int T, int E, int k,
+                         float* out, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(x, Wr, br, LayerWeights{w13, b13, w2, b2}, T, E, k, out, ws, ws_bytes, stream,
+                      false);
 }
 
 moe_status_t moe_forward_mx6(const uint16_t* x, const float* Wr, const float* br,
-                             const uint8_t* w13_codes, const uint8_t* w13_scales,
-                             const uint16_t* b13, const uint8_t* w2_codes,
-                             const uint8_t* w2_scales, const uint16_t* b2, int T, int E, int k,
+                             const moe_packed_weight_t* w13, const uint16_t* b13,
+                             const moe_packed_weight_t* w2, const uint16_t* b2, int T, int E, int k,
                              float* out, void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(x, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, E, k, out,
-                      ws, ws_bytes, stream, true);
+  return forward_impl(x, Wr, br, LayerWeights{w13, b13, w2, b2}, T, E, k, out, ws, ws_bytes, stream,
+                      true);
 }
 
 moe_status_t moe_rmsnorm(const uint16_t* x, const float* scale, float eps, int T, uint16_t* t,
@@ -403,25 +441,25 @@ moe_status_t moe_rmsnorm(const uint16_t* x, const float* scale, float eps, int T
 }
 
 moe_status_t moe_forward_block(const uint16_t* x, const float* norm_scale, float norm_eps,
-                               const float* Wr, const float* br, const uint8_t* w13_codes,
-                               const uint8_t* w13_scales, const uint16_t* b13,
-                               const uint8_t* w2_codes, const uint8_t* w2_scales,
+                               const float* Wr, const float* br, const moe_packed_weight_t* w13,
+                               const uint16_t* b13, const moe_packed_weight_t* w2,
                                const uint16_t* b2, int T, int E, int k, float* out, void* ws,
                                size_t ws_bytes, void* stream) {
   if (!sizes_ok(T, E, k) || !(norm_eps >= 0.f) || !(norm_eps < 1e30f)) return MOE_ERROR_INVALID_VALUE;
   if (T == 0) return MOE_SUCCESS;
   if (!x || !norm_scale || !Wr || !br || !out) return MOE_ERROR_INVALID_VALUE;
-  MOE_TRY(check_weights(w13_codes, w13_scales, b13, w2_codes, w2_scales, b2));
+  MOE_TRY(check_weights(w13, b13, w2, b2, E));
   if (!aligned(x, 16) || !aligned(norm_scale, 16) || !aligned(Wr, 16) || !aligned(out, 16) ||
       !aligned(br, 4))
     return MOE_ERROR_MISALIGNED;
-  MOE_TRY(check_ws(ws, ws_bytes, T, E, k));
+  MOE_TRY(check_ws(ws, ws_bytes, MOE_OP_FORWARD_BLOCK, T, E, k));
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* t = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + layout(T, E, k).xnorm);
+  const WsLayout l = layout(MOE_OP_FORWARD_BLOCK, T, E, k);
+  uint16_t* t = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + l.xnorm);
   MOE_TRY(after_launch(moe::launch_rmsnorm(x, norm_scale, norm_eps, T, t, s), s));
-  return forward_launch(t, Wr, br, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, E, k, out,
-                        ws, s, false, x);
+  return forward_launch(t, Wr, br, LayerWeights{w13, b13, w2, b2}, T, E, k, out,
+                        static_cast<char*>(ws), l, s, false, x);
 }
 
 moe_status_t moe_encode_mx6(const uint16_t* x, int rows, uint8_t* records, void* stream) {

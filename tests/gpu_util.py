@@ -18,7 +18,7 @@ NEAR_TIE_GAP = 1e-4
 
 def to_device(inp, device="cuda", pack=True):
     """Host arrays -> device tensors; with `pack`, the expert weights are also
-    packed on the GPU (keys p13c, p13s, p2c, p2s)."""
+    packed on the GPU (key "experts", a PackedExperts)."""
     import sparse_moe_ffn_fp32_amd as moe
     d = {}
     for key, a in inp.items():
@@ -26,14 +26,14 @@ def to_device(inp, device="cuda", pack=True):
             a = a.view(np.int16)
         d[key] = torch.from_numpy(np.ascontiguousarray(a)).to(device)
     if pack and "w13_codes" in d:
-        d["p13c"], d["p13s"], d["p2c"], d["p2s"] = moe.pack_expert_weights(
-            d["w13_codes"], d["w13_scales"], d["w2_codes"], d["w2_scales"])
+        d["experts"] = moe.pack_experts(d["w13_codes"], d["w13_scales"], d["b13"],
+                                        d["w2_codes"], d["w2_scales"], d["b2"])
     return d
 
 
 def weights_args(d):
-    """Packed expert weights in the argument order of the layer calls."""
-    return (d["p13c"], d["p13s"], d["b13"], d["p2c"], d["p2s"], d["b2"])
+    """The packed expert weights, as the layer calls take them."""
+    return (d["experts"],)
 
 
 def pack_reference(codes: np.ndarray, scales: np.ndarray):
@@ -97,3 +97,60 @@ def check_routing(ids_gpu, w_gpu, logits64, k):
     w_ref = oracle.routing_weights(logits64, ids_gpu.astype(np.int64))
     assert np.max(np.abs(w_gpu - w_ref)) < 2e-5, np.max(np.abs(w_gpu - w_ref))
     return int((~same).sum())
+
+
+def expert_edge_tokens(ids: np.ndarray, E: int) -> np.ndarray:
+    """The tokens that own each expert's first and last routed slot (slot
+    order t*k + j): with the stable expert-sorted order these are the first
+    and last rows of every expert's range, so its first tile and its ragged
+    last tile are both checked."""
+    flat = np.asarray(ids).reshape(-1)
+    k = ids.shape[1]
+    toks = []
+    for e in range(E):
+        where = np.nonzero(flat == e)[0]
+        if where.size:
+            toks += [where[0] // k, where[-1] // k]
+    return np.unique(np.asarray(toks, dtype=np.int64))
+
+
+def oracle_for_gpu_routing(inp, k, ref, ids_gpu, T):
+    """Oracle outputs (out [T, H] and per-slot y [T, k, H] in the GPU's slot
+    order) for the first T tokens of `inp`, from one shared oracle run `ref`
+    (oracle.forward(inp, k, keep_y=True) over all tokens). Tokens whose GPU
+    expert set differs from the oracle's (near ties only, checked by
+    check_routing) are recomputed with the GPU's set."""
+    ids_ref = ref["ids"][:T]
+    out = ref["out"][:T].copy()
+    y = np.empty((T, k, ref["y"].shape[2]), dtype=np.float64)
+    redo = []
+    for t in range(T):
+        if set(ids_gpu[t].tolist()) != set(ids_ref[t].tolist()):
+            redo.append(t)
+            continue
+        pos = {int(e): j for j, e in enumerate(ids_ref[t])}
+        for j in range(k):
+            y[t, j] = ref["y"][t, pos[int(ids_gpu[t, j])]]
+    if redo:
+        full = np.array(ref["ids"])
+        full[:T] = ids_gpu
+        r2 = oracle.forward(inp, k, tokens=np.asarray(redo), ids_override=full, keep_y=True)
+        out[redo] = r2["out"]
+        y[redo] = r2["y"]
+    return out, y
+
+
+_ORACLE_CASES = {}
+
+
+def oracle_case(T, E, k, seed):
+    """(inputs, oracle.forward(inputs, k, keep_y=True)) of make_layer_inputs(T,
+    E, k, seed), computed once per process for the most recent key (large
+    cases are shared between test modules)."""
+    from moe_inputs import make_layer_inputs
+    key = (T, E, k, seed)
+    if key not in _ORACLE_CASES:
+        _ORACLE_CASES.clear()
+        inp = make_layer_inputs(T, E, k, seed=seed)
+        _ORACLE_CASES[key] = (inp, oracle.forward(inp, k, keep_y=True))
+    return _ORACLE_CASES[key]

@@ -14,7 +14,8 @@ import oracle
 import oracle.mx_pieces as mp
 import sparse_moe_ffn_fp32_amd as moe
 from moe_inputs import LAYER_CONFIGS, bf16_bits_from_f32, make_config_inputs, make_layer_inputs
-from tests.gpu_util import assert_out_close, check_routing, out_metrics, to_device, weights_args
+from tests.gpu_util import (assert_out_close, check_routing, expert_edge_tokens, oracle_case,
+                            oracle_for_gpu_routing, out_metrics, to_device, weights_args)
 
 pytestmark = pytest.mark.gpu
 
@@ -129,8 +130,7 @@ def test_forward_mx6_edge_inputs():
     the bar: at [-20, 4] max|err| reaches 5e-2 of RMS in the oracle's own
     emulation of the encoding. moe_forward is exact there.)"""
     cases = [("hot expert", 400, 4, 1, dict(), 2),
-             ("scale range", 640, 8, 4, dict(scale_exp_range=(-16, 0)), None),
-             ("E=256 k=8", 800, 256, 8, dict(), None)]
+             ("scale range", 640, 8, 4, dict(scale_exp_range=(-16, 0)), None)]
     for label, T, E, k, kw, hot in cases:
         say(f"forward_mx6 {label} T={T} E={E} k={k}")
         inp = make_layer_inputs(T, E, k, seed=61 + T, **kw)
@@ -142,10 +142,20 @@ def test_forward_mx6_edge_inputs():
         torch.cuda.synchronize()
         if hot is not None:
             assert np.all(np_(ids)[:, 0] == hot)
-        tokens = np.array([0, 1, T // 2, T - 1]) if E > 64 else None
-        ref = oracle.forward(inp, k, tokens=tokens, ids_override=np_(ids))
-        got = np_(out)[tokens] if tokens is not None else np_(out)
-        assert_out_close(got, ref["out"], label)
+        ref = oracle.forward(inp, k, ids_override=np_(ids))
+        assert_out_close(np_(out), ref["out"], label)
+    # the largest expert count and top-k, every row (the oracle run is shared
+    # with the bf16 path's test of the same inputs)
+    T, E, k = 800, 256, 8
+    say(f"forward_mx6 E=256 k=8 T={T}")
+    inp, ref = oracle_case(T, E, k, seed=4000 + T)
+    d = to_device(inp)
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+    out = moe.forward_mx6(d["x"], d["Wr"], d["br"], *weights_args(d), k=k)
+    torch.cuda.synchronize()
+    check_routing(np_(ids), np_(w), ref["logits"], k)
+    want, _ = oracle_for_gpu_routing(inp, k, ref, np_(ids), T)
+    assert_out_close(np_(out), want, "E=256 k=8")
 
 
 @pytest.mark.parametrize("idx", [2, 3, 4])
@@ -163,7 +173,8 @@ def test_forward_mx6_config_sampled(idx):
     m_all = out_metrics(np_(out), np_(out_bf16).astype(np.float64))
     assert m_all["max_err_over_rms"] < 2e-2 and m_all["mean_rel_l2"] < 5e-3, m_all
     rng = np.random.default_rng(100 + idx)
-    sample = np.unique(np.concatenate([[0, c.T - 1], rng.choice(c.T, 62, replace=False)]))
+    edges = expert_edge_tokens(ids_h, c.E)   # every expert's first and ragged last tile
+    sample = np.unique(np.concatenate([[0, c.T - 1], edges, rng.choice(c.T, 62, replace=False)]))
     ref = oracle.forward(inp, c.k, tokens=sample, ids_override=ids_h)
     m = assert_out_close(np_(out)[sample], ref["out"], c.name)
     say(f"  sampled metrics {m}; mx6 vs bf16 path, all rows {m_all}")
@@ -179,10 +190,9 @@ def test_gate_up_mx6(T, E, k):
     d = to_device(inp)
     ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
     counts, offsets, rows = moe.permute(ids, E)
-    p13c, p13s, b13, _, _, _ = weights_args(d)
     xrec = moe.encode_mx6(d["x"])
-    h = moe.gate_up_mx6(xrec, offsets, rows, p13c, p13s, b13, k=k)
-    h_bf16 = moe.gate_up(d["x"], offsets, rows, p13c, p13s, b13, k=k)
+    h = moe.gate_up_mx6(xrec, offsets, rows, d["experts"], k=k)
+    h_bf16 = moe.gate_up(d["x"], offsets, rows, d["experts"], k=k)
     torch.cuda.synchronize()
     x64 = oracle.bf16_to_f64(inp["x"])
     h_got = oracle.bf16_to_f64(np_(h).view(np.uint16))
