@@ -3,15 +3,18 @@
 moe_forward allocates nothing, keeps no state and issues no memsets, so a
 whole step (router, permutation, both expert GEMMs, combine) can be captured
 once and replayed; this checks that every replay, with eager work of the
-same stream in between, reproduces the eager result.
+same stream in between, reproduces the eager result bit for bit, and that
+the replayed output meets the layer's bar against the oracle.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
+import oracle.block as ob
 import sparse_moe_ffn_fp32_amd as moe
 from moe_inputs import make_layer_inputs
-from tests.gpu_util import to_device, weights_args
+from tests.gpu_util import assert_out_close, check_routing, to_device, weights_args
 
 pytestmark = pytest.mark.gpu
 
@@ -67,3 +70,17 @@ def test_forward_graph_replays(T, E, k, path):
         got = out.clone()
         assert torch.isfinite(got).all(), f"replay {r}: non-finite"
         assert torch.equal(got, eager), f"replay {r} differs"
+    # the replayed output against the oracle (the block: out - x against the
+    # oracle's block on its own normed input)
+    torch.cuda.synchronize()
+    if path == "block":
+        t = moe.rmsnorm(d["x"], g)
+        ids, w = moe.route(t, d["Wr"], d["br"], k=k)
+        ref = ob.block_forward(inp, k, np.full(2880, 1.5, dtype=np.float32), ids_override=ids.cpu().numpy())
+        x64 = oracle.bf16_to_f64(inp["x"])
+        assert_out_close(got.cpu().numpy() - x64, ref["out"] - x64, "graph replay, block")
+    else:
+        ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+        ref = oracle.forward(inp, k, ids_override=ids.cpu().numpy())
+        check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["logits"], k)
+        assert_out_close(got.cpu().numpy(), ref["out"], f"graph replay, {path}")

@@ -15,8 +15,9 @@ import torch
 import oracle
 import sparse_moe_ffn_fp32_amd as moe
 from moe_inputs import LAYER_CONFIGS, make_config_inputs, make_layer_inputs
-from tests.gpu_util import (assert_out_close, check_routing, out_metrics, pack_reference,
-                            to_device, weights_args)
+from tests.gpu_util import (assert_out_close, check_routing, expert_edge_tokens, oracle_case,
+                            oracle_for_gpu_routing, out_metrics, pack_reference, to_device,
+                            weights_args)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,13 +52,15 @@ def test_pack_weights_layout(E, N):
     rng = np.random.default_rng(E * 1000 + N)
     codes = rng.integers(0, 256, size=(E, N, 1440), dtype=np.uint8)
     scales = rng.integers(0, 256, size=(E, N, 90), dtype=np.uint8)
-    pc, ps = moe.pack_weights(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+    pw = moe.pack_weights(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
     torch.cuda.synchronize()
+    assert tuple(pw.codes.shape) == (E, N // 64, 92160)
+    assert tuple(pw.scales.shape) == (E, N // 64, 5760)
     want_c, want_s = pack_reference(codes, scales)
-    assert np.array_equal(np_(pc), want_c)
-    assert np.array_equal(np_(ps), want_s)
+    assert np.array_equal(np_(pw.codes).reshape(codes.shape), want_c)
+    assert np.array_equal(np_(pw.scales).reshape(scales.shape), want_s)
     # a pure permutation: the byte histograms are unchanged
-    assert np.array_equal(np.bincount(np_(pc).ravel(), minlength=256),
+    assert np.array_equal(np.bincount(np_(pw.codes).ravel(), minlength=256),
                           np.bincount(codes.ravel(), minlength=256))
 
 
@@ -190,21 +193,73 @@ def test_forward_small(T, E, k):
 
 def test_forward_max_experts_and_topk():
     """E = 256, k = 8 (the largest supported): few tokens through the
-    weight-streaming kernels, and a tiled batch checked on sampled tokens."""
-    for T, E, k, sampled in ((6, 256, 8, False), (800, 256, 8, True)):
+    weight-streaming kernels, and a tiled batch (25 rows per expert) with
+    every row against the oracle."""
+    for T, E, k in ((6, 256, 8), (800, 256, 8)):
         say(f"forward T={T} E={E} k={k}")
-        inp = make_layer_inputs(T, E, k, seed=4000 + T)
+        inp, ref = oracle_case(T, E, k, seed=4000 + T)
         d = to_device(inp)
         ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
         out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=k)
         torch.cuda.synchronize()
         ids_h = np_(ids)
-        logits = oracle.router_logits(inp["x"], inp["Wr"], inp["br"])
-        check_routing(ids_h, np_(w), logits, k)
-        tokens = np.array([0, 1, T // 2, T - 1]) if sampled else None
-        ref = oracle.forward(inp, k, tokens=tokens, ids_override=ids_h)
-        got = np_(out)[tokens] if sampled else np_(out)
-        assert_out_close(got, ref["out"], f"E={E} k={k} T={T}")
+        check_routing(ids_h, np_(w), ref["logits"], k)
+        want, _ = oracle_for_gpu_routing(inp, k, ref, ids_h, T)
+        m = assert_out_close(np_(out), want, f"E={E} k={k} T={T}")
+        say(f"  metrics {m}")
+
+
+# The 120b expert count (E = 128, k = 4) on one input set of 1024 tokens and
+# its prefixes: T*k <= 20*E (T <= 640) takes the weight-streaming kernels
+# (grid.y = 128; one 16-token tile per pass up to 10 mean rows, T <= 320,
+# two above), T = 641 is the first tiled shape, T = 1024 the tiled kernels
+# with 32 mean rows per expert. Every row of every prefix is compared with
+# one oracle run over the 1024 tokens.
+E128_T = (16, 200, 400, 640, 641, 1024)
+
+
+@pytest.fixture(scope="module")
+def e128():
+    inp = make_layer_inputs(max(E128_T), 128, 4, seed=5128)
+    say("oracle over 1024 tokens, E=128 (shared by the E=128 cases)")
+    ref = oracle.forward(inp, 4, keep_y=True)
+    return inp, ref, to_device(inp)
+
+
+def _prefix(d, T):
+    return {key: (v[:T] if key == "x" else v) for key, v in d.items()}
+
+
+@pytest.mark.parametrize("T", E128_T)
+def test_forward_e128(e128, T):
+    inp, ref, dfull = e128
+    say(f"forward T={T} E=128 k=4 ({'tiled' if T * 4 > 20 * 128 else 'weight-streaming'})")
+    d = _prefix(dfull, T)
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=4)
+    out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=4)
+    torch.cuda.synchronize()
+    ids_h = np_(ids)
+    check_routing(ids_h, np_(w), ref["logits"][:T], 4)
+    want, _ = oracle_for_gpu_routing(inp, 4, ref, ids_h, T)
+    m = assert_out_close(np_(out), want, f"E=128 T={T}")
+    say(f"  metrics {m}")
+
+
+@pytest.mark.parametrize("T", (200, 641, 1024))
+def test_expert_ffn_e128(e128, T):
+    """Every routed slot's unweighted expert output (y) against the oracle's."""
+    inp, ref, dfull = e128
+    say(f"expert_ffn T={T} E=128 k=4")
+    d = _prefix(dfull, T)
+    ids, w, counts, offsets, rows = _gpu_route_and_permute(d, 128, 4)
+    y = moe.expert_ffn(d["x"], offsets, rows, *weights_args(d), k=4)
+    out = moe.combine(y, w)
+    torch.cuda.synchronize()
+    ids_h = np_(ids)
+    check_routing(ids_h, np_(w), ref["logits"][:T], 4)
+    want_out, want_y = oracle_for_gpu_routing(inp, 4, ref, ids_h, T)
+    assert_out_close(np_(y).reshape(T * 4, -1), want_y.reshape(T * 4, -1), "y")
+    assert_out_close(np_(out), want_out, "combine")
 
 
 def test_forward_one_expert_takes_all():
@@ -294,8 +349,11 @@ def test_forward_config_full_oracle(idx):
 
 @pytest.mark.parametrize("idx", [2, 3, 4])
 def test_forward_config_sampled(idx):
+    """Full configurations: every expert's first and last routed token (its
+    first tile and its ragged last tile) plus 62 random tokens against the
+    oracle; every row of the one-call layer against the separate calls."""
     c = LAYER_CONFIGS[idx]
-    say(f"forward config {idx} ({c.name}): sampled tokens + fused vs unfused")
+    say(f"forward config {idx} ({c.name}): edge + random tokens vs the oracle")
     inp = make_config_inputs(idx)
     d = to_device(inp)
     ids, w = moe.route(d["x"], d["Wr"], d["br"], k=c.k)
@@ -310,12 +368,19 @@ def test_forward_config_sampled(idx):
     # every row: the one-call layer vs the separate calls (expert_ffn + combine)
     m_all = out_metrics(np_(out), np_(out_unfused).astype(np.float64))
     assert m_all["max_err_over_rms"] < 1e-4, m_all
-    # sampled rows against the oracle (first, last and random tokens)
     rng = np.random.default_rng(idx)
-    sample = np.unique(np.concatenate([[0, c.T - 1], rng.choice(c.T, 62, replace=False)]))
-    ref = oracle.forward(inp, c.k, tokens=sample, ids_override=ids_h)
+    edges = expert_edge_tokens(ids_h, c.E)
+    sample = np.unique(np.concatenate([[0, c.T - 1], edges, rng.choice(c.T, 62, replace=False)]))
+    touched = np.unique(ids_h[sample])
+    assert touched.size == int((np_(counts) > 0).sum()), "every routed expert is sampled"
+    ref = oracle.forward(inp, c.k, tokens=sample, ids_override=ids_h, keep_y=True)
     m = assert_out_close(np_(out)[sample], ref["out"], c.name)
-    say(f"  sampled metrics {m}; fused vs unfused {m_all}; near-tie tokens with another set: {n_tie}")
+    # the sampled rows of the per-slot outputs too (the unfused path's y)
+    ref_y = ref["y"]
+    yg = np_(y).reshape(c.T, c.k, -1)[sample]
+    assert_out_close(yg.reshape(-1, yg.shape[-1]), ref_y.reshape(-1, ref_y.shape[-1]), "y")
+    say(f"  {sample.size} tokens ({edges.size} expert edges) metrics {m}; fused vs unfused "
+        f"{m_all}; near-tie tokens with another set: {n_tie}")
 
 
 @pytest.mark.parametrize("T,E,k", [(16, 32, 4), (30, 8, 4), (256, 8, 4)])
@@ -325,11 +390,10 @@ def test_gate_up_and_down_accumulate_onto_residual(T, E, k):
     inp = make_layer_inputs(T, E, k, seed=3000 + T + E)
     d = to_device(inp)
     ids, w, counts, offsets, rows = _gpu_route_and_permute(d, E, k)
-    p13c, p13s, b13, p2c, p2s, b2 = weights_args(d)
-    h = moe.gate_up(d["x"], offsets, rows, p13c, p13s, b13, k=k)
+    h = moe.gate_up(d["x"], offsets, rows, d["experts"], k=k)
     resid = torch.randn((T, 2880), dtype=torch.float32, device="cuda")
     out = resid.clone()
-    moe.down_accumulate(h, offsets, rows, w, p2c, p2s, b2, out=out, k=k)
+    moe.down_accumulate(h, offsets, rows, w, d["experts"], out=out, k=k)
     torch.cuda.synchronize()
     ref = oracle.forward(inp, k, ids_override=np_(ids))
     assert_out_close(np_(out) - np_(resid).astype(np.float64), ref["out"], "down_accumulate")
