@@ -319,6 +319,27 @@ moe_status_t moe_forward_block(const uint16_t* x, const float* norm_scale, float
 moe_status_t moe_rmsnorm(const uint16_t* x, const float* scale, float eps, int T,
                          uint16_t* t, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same layer and kernels, with the workspace taken from a scratch array the
+ * library holds in device memory (MOE_NOALLOC_SCRATCH_BYTES per GPU, held
+ * until the process ends) instead of a `ws` argument. The call allocates
+ * nothing: on its first call on a device it looks up that device's copy of
+ * the array (hipGetSymbolAddress, with the device current) and keeps the
+ * address. Sizes whose moe_workspace_size_op(MOE_OP_FORWARD, T, E, k) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES are refused with MOE_ERROR_WORKSPACE (up to
+ * about 2,900 routed slots fit: T = 720 at k = 4). Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or graphs replayed concurrently) race and give
+ * undefined results; calls ordered on one stream are safe. No part of the
+ * array needs clearing between calls. Other arguments, output and errors as
+ * moe_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (48u << 20)
+moe_status_t moe_forward_noalloc(const uint16_t* x, const float* Wr, const float* br,
+                                 const moe_packed_weight_t* w13, const uint16_t* b13,
+                                 const moe_packed_weight_t* w2, const uint16_t* b2,
+                                 int T, int E, int k, float* out, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status_t status);
 

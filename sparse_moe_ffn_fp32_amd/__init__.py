@@ -30,7 +30,7 @@ I = 2880
 __all__ = ["MoeError", "PackedWeight", "PackedExperts", "workspace_size", "pack_weights",
            "pack_experts", "route", "permute", "expert_ffn", "gate_up", "down_accumulate",
            "combine", "forward", "forward_mx6", "encode_mx6", "gate_up_mx6", "forward_block",
-           "rmsnorm", "MX6_ROW_BYTES", "H", "I"]
+           "rmsnorm", "forward_noalloc", "MX6_ROW_BYTES", "H", "I"]
 
 MX6_ROW_BYTES = 5888   # two-piece MX FP6 record bytes per activation row
 _GROUP_CODE_BYTES = 64 * (H // 2)    # packed codes of one 64-row group
@@ -321,6 +321,24 @@ def forward_mx6(x, Wr, br, experts: PackedExperts, k: int = 4,
     """The whole layer with the tiled expert GEMMs on the block-scaled FP4 x FP6
     matrix cores (activations as two MX FP6 pieces) -> out fp32 [T, 2880]."""
     return _forward("moe_forward_mx6", "forward_mx6", x, Wr, br, experts, k, out, workspace)
+
+
+def forward_noalloc(x, Wr, br, experts: PackedExperts, out: torch.Tensor,
+                    k: int = 4) -> torch.Tensor:
+    """The whole layer into the caller's out fp32 [T, 2880], with the library's
+    own device scratch instead of a workspace: nothing is allocated, here or in
+    the library (moe_forward_noalloc). Calls that overlap on one GPU race."""
+    T = x.shape[0]
+    E = Wr.shape[0]
+    _dev(x, "x", _BF16, (T, H))
+    _dev(Wr, "Wr", _F32, (E, H))
+    _dev(br, "br", _F32, (E,))
+    ex = _experts(experts, E)
+    _dev(out, "out", _F32, (T, H))
+    _check(_native.lib().moe_forward_noalloc(
+        _ptr(x), _ptr(Wr), _ptr(br), ex.w13.desc(), _ptr(ex.b13), ex.w2.desc(), _ptr(ex.b2),
+        T, E, k, _ptr(out), _stream(x, Wr, br, *ex.tensors(), out)), "moe_forward_noalloc")
+    return out
 
 
 def encode_mx6(x: torch.Tensor) -> torch.Tensor:

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libmoe_mi355x.so")
 EXPORTED = ("moe_workspace_size", "moe_workspace_size_op", "moe_pack_weights", "moe_route", "moe_permute", "moe_expert_ffn",
             "moe_gate_up", "moe_down_accumulate", "moe_combine", "moe_forward",
             "moe_forward_mx6", "moe_encode_mx6", "moe_gate_up_mx6", "moe_forward_block",
-            "moe_rmsnorm", "moe_status_string")
+            "moe_rmsnorm", "moe_forward_noalloc", "moe_status_string")
 
 MOE_SUCCESS = 0
 STATUS_NAMES = {
@@ -29,6 +29,7 @@ STATUS_NAMES = {
 }
 
 MOE_PACKED_TAG = 0x3450584D
+MOE_NOALLOC_SCRATCH_BYTES = 48 << 20
 
 # moe_op_t: the entry points that take a workspace
 OPS = {"route": 0, "permute": 1, "expert_ffn": 2, "forward": 3, "forward_mx6": 4,
@@ -90,5 +91,7 @@ def lib() -> ctypes.CDLL:
     L.moe_forward_block.restype = ST
     L.moe_rmsnorm.argtypes = [P, P, F, I, P, P]
     L.moe_rmsnorm.restype = ST
+    L.moe_forward_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, P, P]
+    L.moe_forward_noalloc.restype = ST
     _lib = L
     return L

@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "moe.h"
 #include "moe_device.h"
@@ -460,6 +461,59 @@ moe_status_t moe_forward_block(const uint16_t* x, const float* norm_scale, float
   MOE_TRY(after_launch(moe::launch_rmsnorm(x, norm_scale, norm_eps, T, t, s), s));
   return forward_launch(t, Wr, br, LayerWeights{w13, b13, w2, b2}, T, E, k, out,
                         static_cast<char*>(ws), l, s, false, x);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The workspace of moe_forward_noalloc: one copy per GPU, in device memory for
+// the life of the process. In host code `noalloc_scratch` only names the
+// symbol; its device address on the current GPU comes from
+// hipGetSymbolAddress and is kept per device.
+static __device__ __align__(256) unsigned char noalloc_scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch array (looked up once per
+// device, with that device current).
+moe_status_t noalloc_scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERROR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERROR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || !p) return MOE_ERROR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_forward_noalloc(const uint16_t* x, const float* Wr, const float* br,
+                                 const moe_packed_weight_t* w13, const uint16_t* b13,
+                                 const moe_packed_weight_t* w2, const uint16_t* b2, int T, int E,
+                                 int k, float* out, void* stream) {
+  if (!sizes_ok(T, E, k)) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !Wr || !br || !out) return MOE_ERROR_INVALID_VALUE;
+  MOE_TRY(check_weights(w13, b13, w2, b2, E));
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(out, 16) || !aligned(br, 4))
+    return MOE_ERROR_MISALIGNED;
+  const WsLayout l = layout(MOE_OP_FORWARD, T, E, k);
+  if (l.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERROR_WORKSPACE;
+  MOE_TRY(check_device());
+  void* ws = nullptr;
+  MOE_TRY(noalloc_scratch_ptr(&ws));
+  return forward_launch(x, Wr, br, LayerWeights{w13, b13, w2, b2}, T, E, k, out,
+                        static_cast<char*>(ws), l, static_cast<hipStream_t>(stream), false, nullptr);
 }
 
 moe_status_t moe_encode_mx6(const uint16_t* x, int rows, uint8_t* records, void* stream) {

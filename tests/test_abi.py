@@ -311,3 +311,25 @@ def test_rmsnorm_validation(L):
     assert n(t=None) == INVALID
     assert n(g=A + 4) == MISALIGNED
     assert n(t=A + 2) == MISALIGNED
+
+
+def test_forward_noalloc_validation(L):
+    """The allocation-free layer: argument checks as moe_forward, and sizes
+    whose workspace exceeds the library's scratch refused before any launch."""
+    def f(T=4, E=32, k=4, x=A, out=A, w13="d"):
+        w13 = desc(E, 5760) if w13 == "d" else w13
+        return L.moe_forward_noalloc(P(x), P(A), P(A), dp(w13), P(A), dp(desc(E, 2880)), P(A),
+                                     T, E, k, P(out), None)
+    assert f(T=0) == OK
+    assert f(T=0, x=None, out=None) == OK
+    assert f(T=-1) == INVALID
+    assert f(k=9) == INVALID
+    assert f(x=None) == INVALID
+    assert f(out=None) == INVALID
+    assert f(w13=None) == INVALID
+    assert f(w13=desc(tag=0)) == LAYOUT
+    assert f(out=A + 8) == MISALIGNED
+    cap = _native.MOE_NOALLOC_SCRATCH_BYTES
+    big = next(T for T in range(512, 4096, 8) if L.moe_workspace_size_op(OPS["forward"], T, 32, 4) > cap)
+    assert f(T=big) == WORKSPACE
+    assert L.moe_workspace_size_op(OPS["forward"], big - 8, 32, 4) <= cap
