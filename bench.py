@@ -319,7 +319,7 @@ def measure(idx, args, dev, steps, warmup, want_kernel=True):
                 roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                         "traffic": measured_traffic(workload),
-                        "kernel": "ffn_wide_kernel<EPI_SWIGLU> (gate/up + SwiGLU)",
+                        "kernel": "ffn_tile_kernel<EPI_SWIGLU> (gate/up + SwiGLU)",
                         "algorithmic_flop_per_launch": alg}
         layer_frac = layer_flop / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
         layer_unit = "of 2.5 PFLOP/s dense bf16 (algorithmic FLOP / step time)"

@@ -12,31 +12,35 @@
 // quantization, MXFP4 tensor packing) in the library's packed order (see
 // moe_pack_weights in moe.h): inside each group of 64 rows, the bytes come in
 // the order the matrix-core lanes consume them, so every weight load of a wave
-// is one contiguous, fully coalesced 1 KiB (16 code bytes per lane). A lane
-// l = 16g + r holds row r of a 16-row tile and MX block 4s + g of K step s,
-// converts its 32 codes to bf16 in registers (v_cvt_scalef32_pk_bf16_fp4,
-// exact for the supported scales) and feeds four 16x16x32 bf16 MFMAs (fp32
-// accumulate). The activation operand supplies the same K range for lane
-// group g, so each MFMA sums over 8 consecutive K of 4 blocks.
+// is contiguous 256-byte runs or better (16 code bytes per lane). Each lane
+// converts its 32 codes of one MX block to bf16 in registers
+// (v_cvt_scalef32_pk_bf16_fp4, exact for the supported scales); the
+// activation operand supplies the same K values, so each MFMA sums over a
+// permutation of K that both operands share.
 //
 // Two schedules:
 //  * weight-streaming ("skinny", few rows per expert: decode). A workgroup
 //    of three waves owns three 64-row groups of one expert and its tokens,
-//    16 at a time; each wave streams its group's code bytes front to back
-//    (non-temporal loads, 3-step register prefetch), and the workgroup loads
-//    each K step's activation tile once into an LDS ring that all three
-//    waves read. In the layer's own schedule the waves find their expert's
-//    slots in the routing ids; through the standalone entry points they read
-//    offsets / sorted_rows.
-//  * tiled ("wide", many rows per expert: prefill). A 256-thread block owns
-//    four 64-row groups x 64 tokens; the gathered activation tile goes
-//    through a double-buffered LDS ring (128 K per step), weights straight to
-//    registers as above; blocks are numbered XCD by XCD. Its block-scaled
-//    variant (ffn_wide6_kernel) reads the activations as two-piece MX FP6
-//    records instead and feeds them, with the packed FP4 weights unconverted,
-//    to the FP4 x FP6 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4).
+//    16 at a time, on 16x16x32 MFMAs (weights the 16-row operand); each wave
+//    streams its group's code bytes front to back (non-temporal loads,
+//    3-step register prefetch), and the workgroup loads each K step's
+//    activation tile once into an LDS ring that all three waves read. In the
+//    layer's own schedule the waves find their expert's slots in the routing
+//    ids; through the standalone entry points they read offsets / sorted_rows.
+//  * tiled (many rows per expert: prefill), ffn_tile_kernel. A block of 8
+//    waves owns 512 weight rows (one 64-row group per wave) x 128 tokens of
+//    one expert, each wave a 64 x 128 tile of 32x32x16 bf16 MFMAs; the
+//    gathered activation rows go global -> LDS by DMA through a 4-stage ring
+//    (three K steps ahead), the weights straight to registers (two steps
+//    ahead). The work (column block, token tile) is split over the 8 XCDs in
+//    equal contiguous ranges. Its block-scaled variant (ffn_wide6_kernel, 4
+//    waves x 64 tokens) reads the activations as two-piece MX FP6 records and
+//    feeds them, with the packed FP4 weights unconverted, to the FP4 x FP6
+//    matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4).
 #include "moe_device.h"
 #include "moe_launch.h"
+
+#include <utility>
 
 namespace moe {
 
@@ -405,16 +409,17 @@ constexpr int kXcds = 8;
 // contiguous range of the work. Within that order, kTileChunk consecutive
 // token tiles go with each weight column block in turn (tiles fastest): the
 // tiles of a chunk read the same weights close together in time on one L2.
+template <int CH = kTileChunk>
 __device__ __forceinline__ void wide_work_item(int gx, int gy, int& wx, int& ty) {
   const int nb = gx * gy;
   const int b = blockIdx.x;
   const int q = nb / kXcds, r = nb % kXcds, xcd = b % kXcds, idx = b / kXcds;
   const int L = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
-  const int per = gx * kTileChunk;
+  const int per = gx * CH;
   const int chunk = L / per, rem = L - chunk * per;
-  const int cy = min(kTileChunk, gy - chunk * kTileChunk);
+  const int cy = min(CH, gy - chunk * CH);
   wx = rem / cy;
-  ty = chunk * kTileChunk + (rem - wx * cy);
+  ty = chunk * CH + (rem - wx * cy);
 }
 constexpr int kWdNT = 4;           // 16-token column tiles per wave
 constexpr int kWdBT = 16 * kWdNT;   // tokens per tile
@@ -451,15 +456,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Block = 4 waves = four 64-row groups x 64 tokens. Activations go straight
+// The block-scaled tiled kernel (activations as two-piece MX FP6 records).
+// Block = 4 waves = four 64-row groups x 64 tokens. The records go straight
 // from global memory into a 2-stage LDS ring (global_load_lds, 16 bytes per
 // lane, no staging registers); within a 256-byte token row the 16-byte
-// pieces are XOR-swizzled by (token & 15), so the 16 token rows read by a
-// fragment load hit distinct banks. Weights stream to registers (2-step
-// ring) as in the skinny kernel. Per K step: wait for this step's loads,
-// barrier, issue the next activation stage, compute, refill the weights.
-template <int EPI, bool W_AS_B, bool MX6>
-__device__ __forceinline__ void wide_body(const FfnArgs& a) {
+// pieces are XOR-swizzled by (token & 15). Weights stream to registers
+// (2-step ring). Per K step: wait for this step's loads, barrier, issue the
+// next activation stage, compute, refill the weights.
+template <int EPI, bool W_AS_B>
+__device__ __forceinline__ void wide6_body(const FfnArgs& a) {
   __shared__ __attribute__((aligned(1024))) uint8_t xs[2 * kXStage];
   __shared__ int slot_of[kWdBT];
   __shared__ uint16_t bias_s[kWdGroups * 64];
@@ -487,31 +492,23 @@ __device__ __forceinline__ void wide_body(const FfnArgs& a) {
 
   // Activation loads: wave w, instruction j fills LDS rows 4*(4w+j) .. +3
   // (1 KiB); lane i takes token t = 4*(4w+j) + (i >> 4) and LDS piece
-  // q = i & 15, which holds K piece q ^ (t & 15). Padded tokens read the
-  // tile's first row (outputs dropped); the K tail re-reads the row's last
-  // piece (weights zero there), so all LDS values are finite.
-  // With MX6 the rows are two-piece FP6 records instead (256 bytes per K
-  // step, complete, so no tail handling); the same swizzle applies.
+  // q = i & 15, which holds record piece q ^ (t & 15). Padded tokens read the
+  // tile's first row (outputs dropped). A record holds a whole K step, so
+  // there is no tail handling.
   const int q_lds = lane & 15;
-  const uint8_t* xbase = MX6 ? a.act6 : reinterpret_cast<const uint8_t*>(a.act);
+  const uint8_t* xbase = a.act6;
   size_t xoff[kXLoads];
-  int xpiece[kXLoads];
 #pragma unroll
   for (int j = 0; j < kXLoads; ++j) {
     const int t = 4 * (kXLoads * wave + j) + (lane >> 4);
     const int p = rb + t < re ? rb + t : rb;
     const int row = a.gather ? a.sorted_rows[p] / a.k : p;
-    xpiece[j] = q_lds ^ (t & 15);
-    xoff[j] = MX6 ? (size_t)row * kRowRecBytes + xpiece[j] * 16 : (size_t)row * (2 * kH);
+    xoff[j] = (size_t)row * kRowRecBytes + (q_lds ^ (t & 15)) * 16;
   }
   auto load_x = [&](uint8_t* dst, int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j) {
-      const uint8_t* src;
-      if constexpr (MX6)
-        src = xbase + xoff[j] + s * kRecBytes;
-      else
-        src = xbase + xoff[j] + 2 * min(s * 128 + xpiece[j] * 8, kH - 8);
+      const uint8_t* src = xbase + xoff[j] + s * kRecBytes;
       __builtin_amdgcn_global_load_lds(
           (const void*)src,
           (__attribute__((address_space(3))) void*)(dst + (kXLoads * wave + j) * 1024), 16, 0, 0);
@@ -532,7 +529,7 @@ __device__ __forceinline__ void wide_body(const FfnArgs& a) {
     for (int nt = 0; nt < kWdNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const uint8_t* xsb, int buf) __attribute__((always_inline)) {
-    if constexpr (MX6) {
+    {
       // Block-scaled FP4 x FP6 (16x16x128): the packed weight lane holds one
       // whole MX block, which is the instruction's operand as it stands; its
       // scale is byte mt of the step's scale dword (the instruction reads
@@ -574,30 +571,6 @@ __device__ __forceinline__ void wide_body(const FfnArgs& a) {
         asm volatile("" : "+v"(acc[0][nt]), "+v"(acc[1][nt]), "+v"(acc[2][nt]), "+v"(acc[3][nt]));
         __builtin_amdgcn_sched_barrier(0);
       }
-      return;
-    }
-    float sf[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sf[mt] = e8m0_to_f32((wsc[buf] >> (8 * mt)) & 0xFFu);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16x8 xf[kWdNT];
-#pragma unroll
-      for (int nt = 0; nt < kWdNT; ++nt) {
-        const int t = 16 * nt + r;
-        xf[nt] = *reinterpret_cast<const bf16x8*>(xsb + t * kXRow + (((4 * g + i) ^ r) * 16));
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 wf = fp4x8_to_bf16x8(dword_of(wq[buf][mt], i), sf[mt]);
-#pragma unroll
-        for (int nt = 0; nt < kWdNT; ++nt) {
-          if constexpr (W_AS_B)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[nt], wf, acc[mt][nt], 0, 0, 0);
-          else
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[nt], acc[mt][nt], 0, 0, 0);
-        }
-      }
     }
   };
 
@@ -626,7 +599,7 @@ __device__ __forceinline__ void wide_body(const FfnArgs& a) {
       }
     }
   }
-  if constexpr (MX6 && !W_AS_B && EPI == EPI_SWIGLU) {
+  if constexpr (!W_AS_B && EPI == EPI_SWIGLU) {
     if (a.h6_out) {
       // h as two-piece MX FP6 records: this wave's 32 h features of a token
       // (group G of 64 interleaved gate/up rows) are MX block G of that
@@ -726,17 +699,389 @@ __device__ __forceinline__ void wide_body(const FfnArgs& a) {
   }
 }
 
-template <int EPI, bool W_AS_B>
-__global__ __launch_bounds__(256) void ffn_wide_kernel(FfnArgs a) {
-  wide_body<EPI, W_AS_B, false>(a);
-}
-
 // The FP6 fragments of four token tiles would otherwise all be loaded ahead
 // of the matrix-core work, leaving room for two waves per SIMD; three keep
 // the load latency covered.
 template <int EPI, bool W_AS_B>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void ffn_wide6_kernel(FfnArgs a) {
-  wide_body<EPI, W_AS_B, true>(a);
+  wide6_body<EPI, W_AS_B>(a);
+}
+
+// ------------------------------------------------------------------ tiled, bf16
+// The many-rows-per-expert schedule of the bf16 path. Block = 8 waves = eight
+// 64-row weight groups (512 rows) x 128 tokens of one expert, two waves per
+// SIMD; each wave owns a 64 x 128 output tile of 32x32x16 bf16 MFMAs (2
+// weight tiles x 4 token tiles, 128 accumulator registers), so every
+// dequantised weight fragment feeds four MFMAs and every activation fragment
+// read from LDS feeds two, and each activation stage serves 512 weight rows.
+//
+// Weights: straight to registers from the packed order. For a 32-row tile mt
+// and K half h of the instruction, lane 32h + c loads row 32mt + c = 16-row
+// tile m = 2mt + (c >> 4), packed lane 16g + (c & 15), MX block g = 2jb + h of
+// the step (jb = 0, 1): four 256-byte runs per load. Dword i of that load
+// (codes 8i .. 8i + 7 of the block) is the lane's 8-value K slice of MFMA
+// (jb, i); the activation operand supplies the same K for its token.
+// Activations: gathered rows go global -> LDS by DMA into a 4-stage ring of
+// 128 rows x 256 bytes (128 K); the 16-byte pieces of a row are XOR-swizzled
+// by (row & 15), so the 32-row operand reads (row c, piece 4(2jb + h) + i)
+// hit 64 distinct banks in every LDS cycle (measured conflict-free).
+// A tile with at most 64 tokens (an expert's last) runs only its first two
+// token tiles.
+constexpr int kTlBT = 128;                       // tokens per tile
+constexpr int kTlWaves = 8;                      // waves per block, one 64-row group each
+constexpr int kTlThreads = 64 * kTlWaves;
+constexpr int kTlRows = 64 * kTlWaves;           // weight rows per block (512)
+constexpr int kTlStage = kTlBT * kXRow;          // 32 KiB per activation stage
+constexpr int kTlStages = 4;                     // activation ring depth (3 steps ahead)
+constexpr int kTlXLoads = kTlStage / (kTlWaves * 1024);  // 1 KiB DMA instructions per wave per stage (4)
+constexpr int kTlChunk = 4;                      // token tiles per pass over a weight column block
+
+// Tiles of `bt` rows over all experts' row ranges (one full wave; every lane
+// gets the same answer).
+__device__ __forceinline__ int count_tiles(const int32_t* __restrict__ offsets, int E, int bt) {
+  const int lane = threadIdx.x & 63;
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane * 4 + q;
+    if (e < E) local += (offsets[e + 1] - offsets[e] + bt - 1) / bt;
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) local += __shfl_xor(local, d, 64);
+  return local;
+}
+
+// Work item (column block wx, token tile ty) of this block, from `total`
+// real tiles: the gx * total items are split into 8 contiguous ranges, one
+// per XCD (blocks are dealt to the XCDs round-robin in launch order); within
+// a range, CHUNK consecutive tiles go with each column block in turn. False
+// for a spare block.
+template <int CHUNK>
+__device__ __forceinline__ bool tile_work_item(int gx, int total, int& wx, int& ty) {
+  const int nw = gx * total;
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds, idx = b / kXcds;
+  const int q = nw / kXcds, r = nw % kXcds;
+  if (idx >= q + (xcd < r ? 1 : 0)) return false;
+  const int L = xcd * q + min(xcd, r) + idx;
+  const int per = gx * CHUNK;
+  const int chunk = L / per, rem = L - chunk * per;
+  const int cy = min(CHUNK, total - chunk * CHUNK);
+  wx = rem / cy;
+  ty = chunk * CHUNK + (rem - wx * cy);
+  return true;
+}
+
+// 16 bytes per lane from global memory straight into LDS at `lds_dst` +
+// 16 * lane (lds_dst wave-uniform). Written as inline asm: the compiler then
+// does not treat the DMA as an LDS write, so it issues no wait for it before
+// the LDS reads of the other stages (it would otherwise wait for every
+// outstanding load there); completion is tracked by the caller's vmcnt waits.
+// The instruction has no register result.
+__device__ __forceinline__ void lds_dma16(const void* src, const uint8_t* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+}
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, each call its own code
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+struct TlStep {
+  uint4 w[2][2];    // [jb][mt]
+  uint32_t sc[2];   // [jb]: scale bytes of 16-row tiles m = 0..3 for this lane's (g, r)
+};
+
+struct TlWeights {
+  const uint8_t* cg;
+  const uint8_t* sg;
+  int lane_c, lane_c_last, lane_s;   // byte offsets of this lane inside a step
+  __device__ __forceinline__ void init(const FfnArgs& a, int e, int G, int lane) {
+    const size_t grp = (size_t)e * (a.N >> 6) + G;
+    cg = a.codes + grp * kGroupCodeBytes;
+    sg = a.scales + grp * kGroupScaleBytes;
+    const int h = lane >> 5, c = lane & 31;
+    const int mhi = c >> 4, rr = c & 15;
+    lane_c = mhi * 1024 + (16 * h + rr) * 16;
+    lane_c_last = mhi * 512 + (16 * h + rr) * 16;
+    lane_s = (16 * h + rr) * 4;
+  }
+  // half jb of step s: codes of both 32-row tiles and the scale dword (the
+  // half last step has only jb = 0); 3 loads
+  __device__ __forceinline__ void load_half(int s, int jb, TlStep& st) const {
+    // the step's offsets are made opaque so that each step computes its own
+    // addresses (hoisted, 23 steps' worth of 64-bit addresses would not fit
+    // beside the accumulators)
+    int co = s * kStepCodeBytes, so = s * 256;
+    asm volatile("" : "+s"(co), "+s"(so));
+    if (s < kFullSteps) {
+      const uint8_t* c = cg + co + lane_c;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        st.w[jb][mt] = *reinterpret_cast<const uint4*>(c + mt * 2048 + jb * 512);
+      st.sc[jb] = *reinterpret_cast<const uint32_t*>(sg + so + lane_s + jb * 128);
+    } else if (jb == 0) {
+      const uint8_t* c = cg + co + lane_c_last;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) st.w[0][mt] = *reinterpret_cast<const uint4*>(c + mt * 1024);
+      st.sc[0] = *reinterpret_cast<const uint32_t*>(sg + so + lane_s);
+    }
+  }
+};
+
+// The vmcnt each K step s waits for before its barrier (between substeps 3
+// and 4): the next step's stage X(s+1) and this step's second weight half
+// W(s) half 1 must have landed; everything issued after W(s) half 1 may stay
+// in flight. Issue order: prologue W(0), W(1), X(0), X(1), X(2); step s,
+// after its barrier: W(s+2) half 0, X(s+3) (substeps 4..7), W(s+2) half 1
+// (after substep 7). X(s+1) goes before W(s) half 1 (both in step s - 2),
+// except that X(1), X(2) are prologue loads.
+__host__ __device__ constexpr int tl_issued_after_barrier(int s) {
+  return (s + 2 < kSteps ? 3 : 0) + (s + 3 < kSteps ? kTlXLoads : 0) + (s + 2 < kSteps - 1 ? 3 : 0);
+}
+__host__ __device__ constexpr int tl_wait_mid(int s) {
+  return s == 0 ? kTlXLoads                        // X(2)
+       : s == 1 ? tl_issued_after_barrier(0)       // after X(2): step 0's loads
+       : tl_issued_after_barrier(s - 1);
+}
+
+template <int EPI, int NTA, bool W_OK>
+__device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const int* slot_of,
+                                         int* xrow_of, const uint16_t* bias_s, int e, int G,
+                                         int rb, int re) {
+  constexpr bool w_ok = W_OK;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31;
+  const int rr = c & 15, mhi = c >> 4;
+
+  // Activation DMA: wave w, instruction j fills token rows 4(4w + j) .. + 3
+  // of a stage; lane i takes row t = 4(4w + j) + (i >> 4) and LDS piece
+  // q = i & 15, which holds K piece q ^ (t & 15). Padded rows read the tile's
+  // first row; the K tail (last step, pieces past the row) re-reads the row's
+  // last piece. The instructions whose rows lie in token tiles a half tile
+  // skips are not issued.
+  const int q_lds = lane & 15;
+  constexpr int kLoadRows = NTA * 32;
+  const uint16_t* xsrc[kTlXLoads];   // this lane's row (and K piece) per instruction
+#pragma unroll
+  for (int j = 0; j < kTlXLoads; ++j) {
+    const int t = 4 * (kTlXLoads * wave + j) + (lane >> 4);
+    const int kp = (q_lds ^ ((4 * j + (lane >> 4)) & 15)) * 8;   // t & 15 = (4j + (lane >> 4)) & 15
+    xsrc[j] = a.act + (size_t)xrow_of[t] * kH + kp;
+  }
+  auto load_x_one = [&](uint8_t* dst, int s, int j) __attribute__((always_inline)) {
+    if (4 * (kTlXLoads * wave + j) >= kLoadRows) return;   // wave-uniform
+    int ko = s * 128;
+    asm volatile("" : "+s"(ko));
+    const uint16_t* src = xsrc[j] + ko;
+    if (s == kSteps - 1) {
+      // pieces past the row's end: its last piece instead
+      const uint16_t* row_end = xsrc[j] - ((q_lds ^ ((4 * j + (lane >> 4)) & 15)) * 8) + kH - 8;
+      src = src > row_end ? row_end : src;
+    }
+    lds_dma16(src, dst + (kTlXLoads * wave + j) * 1024);
+  };
+  auto stage = [&](int s) __attribute__((always_inline)) {
+    int so = (s & (kTlStages - 1)) * kTlStage;
+    asm volatile("" : "+s"(so));
+    return xs + so;
+  };
+
+  TlWeights wsrc;
+  wsrc.init(a, e, w_ok ? G : 0, lane);
+  TlStep wq[2];
+  f32x16 acc[2][NTA];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTA; ++nt) acc[mt][nt] = f32x16{};
+
+  // One K step: 8 substeps (jb, i) of 2 x NTA MFMAs each. The activation DMA
+  // of step s + 3 and the weights of step s + 2 (into this step's register
+  // slot, half by half once each half has been consumed) are spread over the
+  // substeps, so the wave keeps the matrix cores fed while its memory
+  // instructions wait to issue.
+  auto read_x = [&](const uint8_t* xsb, int q, bf16x8 (&xf)[NTA]) __attribute__((always_inline)) {
+    const int jb = q >> 2, i = q & 3;
+#pragma unroll
+    for (int nt = 0; nt < NTA; ++nt)
+      xf[nt] = *reinterpret_cast<const bf16x8*>(xsb + (32 * nt + c) * kXRow +
+                                                (((8 * jb + 4 * h + i) ^ rr) * 16));
+  };
+  auto wait_for = [&](int n) __attribute__((always_inline)) {
+    switch (n) {
+      case 0: wait_vmcnt<0>(); break;
+      case 3: wait_vmcnt<3>(); break;
+      case 4: wait_vmcnt<4>(); break;
+      case 8: wait_vmcnt<8>(); break;
+      case 10: wait_vmcnt<10>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
+  };
+
+  // One K step: 8 substeps q = (jb, i) of 2 x NTA MFMAs each (the half last
+  // step: 4). The block synchronises once per step, between substeps 3 and 4:
+  // by then every wave has waited for its own DMA of the next step's stage
+  // (so that stage is complete) and has finished reading the stage of the
+  // previous step (so the DMA of step s + 3 may refill it: it is issued in
+  // substeps 4..7). The next step's first activation fragments are read at
+  // the end of the step, so no step starts with an LDS wait. The weights of
+  // step s + 2 refill this step's register slot half by half, as each half
+  // is consumed.
+  bf16x8 xf[NTA];
+  auto kstep = [&](int s, TlStep& st) __attribute__((always_inline)) {
+    const uint8_t* xsb = stage(s);
+    const int nq = s == kSteps - 1 ? 4 : 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q >= nq) break;
+      const int jb = q >> 2, i = q & 3;
+      bf16x8 wf[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const float sf = e8m0_to_f32((st.sc[jb] >> (8 * (2 * mt + mhi))) & 0xFFu);
+        wf[mt] = fp4x8_to_bf16x8(dword_of(st.w[jb][mt], i), sf);
+      }
+      // fragment nt of the next substep (or of the next step's first, once
+      // the block has passed this step's barrier) is read into xf[nt] as
+      // soon as this substep's two MFMAs on it are issued
+      const bool next_here = q + 1 < nq;
+      const bool next_step = q == nq - 1 && s + 1 < kSteps;
+#pragma unroll
+      for (int nt = 0; nt < NTA; ++nt) {
+        if (w_ok) {
+          acc[0][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0], xf[nt], acc[0][nt], 0, 0, 0);
+          acc[1][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1], xf[nt], acc[1][nt], 0, 0, 0);
+        }
+        if (next_here || next_step) {
+          const uint8_t* src = next_here ? xsb : stage(s + 1);
+          const int qn = next_here ? q + 1 : 0;
+          xf[nt] = *reinterpret_cast<const bf16x8*>(src + (32 * nt + c) * kXRow +
+                                                    (((8 * (qn >> 2) + 4 * h + (qn & 3)) ^ rr) * 16));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (q == 3) {
+        if (s + 1 < kSteps) {
+          wait_for(tl_wait_mid(s));
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (s + 2 < kSteps) wsrc.load_half(s + 2, 0, st);
+      }
+      if (q >= 4 && s + 3 < kSteps) load_x_one(stage(s + 3), s + 3, q - 4);
+      if (q == 7 && s + 2 < kSteps) wsrc.load_half(s + 2, 1, st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  wsrc.load_half(0, 0, wq[0]);
+  wsrc.load_half(0, 1, wq[0]);
+  wsrc.load_half(1, 0, wq[1]);
+  wsrc.load_half(1, 1, wq[1]);
+#pragma unroll
+  for (int s = 0; s < kTlStages - 1; ++s)
+#pragma unroll
+    for (int j = 0; j < kTlXLoads; ++j) load_x_one(stage(s), s, j);
+  wait_for(2 * kTlXLoads);   // X(0) and both weight steps
+  __builtin_amdgcn_s_barrier();
+  read_x(stage(0), 0, xf);
+  // every step is its own straight-line code (compile-time step index): the
+  // waits, ring slots and stage offsets are constants, and the compiler's own
+  // load accounting stays exact
+  static_for<kSteps>([&](auto S) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value;
+    kstep(s, wq[s & 1]);
+  });
+  static_assert(tl_wait_mid(0) == 4 && tl_wait_mid(1) == 10 && tl_wait_mid(10) == 10 &&
+                tl_wait_mid(20) == 10 && tl_wait_mid(21) == 3, "load accounting");
+  if (!w_ok) return;
+
+  // D[weight row][token]: lane holds token column c of tile nt and weight
+  // rows 32mt + 8q + 4h + j (j = 0..3) of the wave's group
+#pragma unroll
+  for (int nt = 0; nt < NTA; ++nt) {
+    const int t = 32 * nt + c;
+    if (rb + t >= re) continue;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lr = 32 * mt + 8 * q + 4 * h;   // row within the group
+        const f32x16& A = acc[mt][nt];
+        const float v0 = A[4 * q + 0] + bf16_bits_to_f32(bias_s[wave * 64 + lr + 0]);
+        const float v1 = A[4 * q + 1] + bf16_bits_to_f32(bias_s[wave * 64 + lr + 1]);
+        const float v2 = A[4 * q + 2] + bf16_bits_to_f32(bias_s[wave * 64 + lr + 2]);
+        const float v3 = A[4 * q + 3] + bf16_bits_to_f32(bias_s[wave * 64 + lr + 3]);
+        const int R0 = G * 64 + lr;
+        if constexpr (EPI == EPI_SWIGLU) {
+          const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(v0, v1));
+          const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(v2, v3));
+          *reinterpret_cast<uint32_t*>(a.h_out + (size_t)(rb + t) * kI + R0 / 2) = h0 | (h1 << 16);
+        } else if constexpr (EPI == EPI_COMBINE) {
+          const int slot = slot_of[t];
+          const float wt = a.topk_w[slot];
+          float* o = a.out + (size_t)(slot / a.k) * kH + R0;
+          unsafeAtomicAdd(o + 0, wt * v0);
+          unsafeAtomicAdd(o + 1, wt * v1);
+          unsafeAtomicAdd(o + 2, wt * v2);
+          unsafeAtomicAdd(o + 3, wt * v3);
+        } else {
+          *reinterpret_cast<float4*>(a.y_out + (size_t)slot_of[t] * kH + R0) = make_float4(v0, v1, v2, v3);
+        }
+      }
+    }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kTlThreads) __attribute__((amdgpu_waves_per_eu(2))) void ffn_tile_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[kTlStages * kTlStage];
+  __shared__ int slot_of[kTlBT];
+  __shared__ int xrow_of[kTlBT];
+  __shared__ uint16_t bias_s[kTlRows];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int gx = ((a.N >> 6) + kTlWaves - 1) / kTlWaves;
+  int wx, ty, e, rb, re;
+  // The grid holds an upper bound of the tiles; the real work (gx column
+  // blocks x the experts' tiles) is dealt to the 8 XCDs in equal contiguous
+  // ranges, so the spare blocks of the bound spread over all XCDs instead of
+  // leaving the last ones idle.
+  const int total = count_tiles(a.offsets, a.E, kTlBT);
+  if (!tile_work_item<kTlChunk>(gx, total, wx, ty)) return;
+  find_tile(a.offsets, a.E, kTlBT, ty, e, rb, re);
+  const int G = wx * kTlWaves + wave;
+  const bool w_ok = G < (a.N >> 6);
+  const int nvalid = re - rb;
+  if (tid < kTlBT) slot_of[tid] = tid < nvalid ? a.sorted_rows[rb + tid] : -1;
+  {
+    const int row = wx * kTlRows + tid;
+    bias_s[tid] = row < a.N ? a.bias[(size_t)e * a.N + row] : 0;
+  }
+  __syncthreads();
+  // activation row of each token row of the tile (padded rows: the first)
+  if (tid < kTlBT) {
+    const int tv = tid < nvalid ? tid : 0;
+    xrow_of[tid] = a.gather ? slot_of[tv] / a.k : rb + tv;
+  }
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(w_ok ? 1 : 0)) {
+    if (nvalid > 64) tile_run<EPI, 4, true>(a, xs, slot_of, xrow_of, bias_s, e, G, rb, re);
+    else tile_run<EPI, 2, true>(a, xs, slot_of, xrow_of, bias_s, e, G, rb, re);
+  } else {
+    if (nvalid > 64) tile_run<EPI, 4, false>(a, xs, slot_of, xrow_of, bias_s, e, G, rb, re);
+    else tile_run<EPI, 2, false>(a, xs, slot_of, xrow_of, bias_s, e, G, rb, re);
+  }
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -771,10 +1116,12 @@ hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s)
       }
       return hipGetLastError();
     }
+    const int tl_tiles = (n_rows + kTlBT - 1) / kTlBT + min(a.E, n_rows);
+    const dim3 tl_grid(((groups + kTlWaves - 1) / kTlWaves) * tl_tiles);
     switch (epi) {
-      case EPI_SWIGLU: hipLaunchKernelGGL((ffn_wide_kernel<EPI_SWIGLU, false>), grid, dim3(256), 0, s, a); break;
-      case EPI_COMBINE: hipLaunchKernelGGL((ffn_wide_kernel<EPI_COMBINE, true>), grid, dim3(256), 0, s, a); break;
-      default: hipLaunchKernelGGL((ffn_wide_kernel<EPI_STORE_Y, true>), grid, dim3(256), 0, s, a); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((ffn_tile_kernel<EPI_SWIGLU>), tl_grid, dim3(kTlThreads), 0, s, a); break;
+      case EPI_COMBINE: hipLaunchKernelGGL((ffn_tile_kernel<EPI_COMBINE>), tl_grid, dim3(kTlThreads), 0, s, a); break;
+      default: hipLaunchKernelGGL((ffn_tile_kernel<EPI_STORE_Y>), tl_grid, dim3(kTlThreads), 0, s, a); break;
     }
   }
   return hipGetLastError();
