@@ -328,13 +328,13 @@ moe_status_t moe_rmsnorm(const uint16_t* x, const float* scale, float eps, int T
  * the array (hipGetSymbolAddress, with the device current) and keeps the
  * address. Sizes whose moe_workspace_size_op(MOE_OP_FORWARD, T, E, k) exceeds
  * MOE_NOALLOC_SCRATCH_BYTES are refused with MOE_ERROR_WORKSPACE (up to
- * about 2,900 routed slots fit: T = 720 at k = 4). Every
+ * about 3,100 routed slots fit: T = 784 at k = 4 for any E). Every
  * call on one GPU shares that GPU's array: calls that overlap on one GPU (on
  * different streams, or graphs replayed concurrently) race and give
  * undefined results; calls ordered on one stream are safe. No part of the
  * array needs clearing between calls. Other arguments, output and errors as
  * moe_forward. */
-#define MOE_NOALLOC_SCRATCH_BYTES (48u << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES (56u << 20)
 moe_status_t moe_forward_noalloc(const uint16_t* x, const float* Wr, const float* br,
                                  const moe_packed_weight_t* w13, const uint16_t* b13,
                                  const moe_packed_weight_t* w2, const uint16_t* b2,

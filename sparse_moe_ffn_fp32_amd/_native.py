@@ -29,7 +29,7 @@ STATUS_NAMES = {
 }
 
 MOE_PACKED_TAG = 0x3450584D
-MOE_NOALLOC_SCRATCH_BYTES = 48 << 20
+MOE_NOALLOC_SCRATCH_BYTES = 56 << 20
 
 # moe_op_t: the entry points that take a workspace
 OPS = {"route": 0, "permute": 1, "expert_ffn": 2, "forward": 3, "forward_mx6": 4,

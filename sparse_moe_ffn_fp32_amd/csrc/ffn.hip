@@ -40,7 +40,6 @@
 #include "moe_device.h"
 #include "moe_launch.h"
 
-#include <utility>
 
 namespace moe {
 
@@ -782,16 +781,6 @@ __device__ __forceinline__ void lds_dma16(const void* src, const uint8_t* lds_ds
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_dst);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
-}
-
-template <class F, int... I>
-__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-// f(integral_constant<int, i>) for i = 0 .. N-1, each call its own code
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 struct TlStep {

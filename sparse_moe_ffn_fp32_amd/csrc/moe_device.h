@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace moe {
 
 constexpr int kH = 2880;            // hidden_size (GPT-OSS raw config.json fields)
@@ -236,6 +238,17 @@ __device__ __forceinline__ void mx6x2_encode(const float (&v)[32], uint32_t (&w1
   for (int j = 0; j < 32; ++j) v0[j] = v[j] + 0.0f;   // -0.0 -> +0.0
   if (!mx6_encode_piece_cvt(v0, w1, s1, r1)) mx6_encode_piece(v0, w1, s1, r1);
   if (!mx6_encode_piece_cvt(r1, w2, s2, r2)) mx6_encode_piece(r1, w2, s2, r2);
+}
+
+// Compile-time loop: f(integral_constant<int, i>) for i = 0 .. N-1, each call
+// its own code (a fully unrolled loop whose steps cannot be merged or rolled).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace moe

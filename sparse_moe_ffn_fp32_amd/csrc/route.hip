@@ -9,7 +9,7 @@
 // exactly into three bf16 pieces (hi + mid + lo, 8 significant bits each).
 // Every product x * piece is exact in fp32 and the matrix core accumulates in
 // fp32, so the result is an fp32-accumulated dot product of the fp32 weights.
-// A wave computes a 32-token x 32*MT-expert tile of 32x32x16 MFMAs over a K
+// A wave computes 32-token x 32*MT-expert tiles of 32x32x16 MFMAs over a K
 // range, with a register prefetch ring over its K steps.
 //
 // Two schedules, chosen by T (both deterministic, fixed summation order):
@@ -18,15 +18,18 @@
 //    launch adds the 20 partials in chunk order, adds the bias and selects
 //    the top k: blocks of 256/E tokens when no permutation is wanted, or a
 //    single 1024-thread block that also builds the expert permutation.
-//  * many tokens: a block per 32 tokens, its waves split K and add their
-//    partial tiles in wave order through LDS, then select the top k and
-//    count the block's routed slots per expert for the parallel permutation.
+//  * many tokens: one launch splits the weights into their bf16 pieces, in
+//    MFMA operand order; then a block per 32 or 64 tokens, its waves split K
+//    and add their partial tiles in wave order through LDS, then select the
+//    top k and count the routed slots per expert of each 32-token group for
+//    the parallel permutation.
 #include "moe_block_permute.h"
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace moe {
 
+constexpr int kRouteSteps = kH / 16;             // MFMA steps of 16 K
 constexpr int kRouteChunks = 20;                  // K chunks of the few-token schedule
 constexpr int kRouteChunkSteps = kH / 16 / kRouteChunks;  // 9 MFMA steps of 16 K
 constexpr int kRouteSmallT = 128;
@@ -35,10 +38,13 @@ static_assert(kRouteChunkSteps * 16 * kRouteChunks == kH, "chunks must tile K");
 
 static bool few_tokens(int T, int E) { return T <= kRouteSmallT && T * E <= kRouteMaxPairs; }
 
+size_t route_split_bytes(int E);
+
 size_t route_scratch_bytes(int T, int E) {
-  // few tokens: K-chunk partial logits; many: per-32-token-block expert histograms
+  // few tokens: K-chunk partial logits; many: the split weights, then the
+  // per-32-token-group expert histograms
   return few_tokens(T, E) ? (size_t)kRouteChunks * T * E * sizeof(float)
-                          : (size_t)((T + 31) / 32) * E * sizeof(int32_t);
+                          : route_split_bytes(E) + (size_t)((T + 31) / 32) * E * sizeof(int32_t);
 }
 
 __device__ __forceinline__ void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
@@ -126,11 +132,11 @@ constexpr int route_depth() {
   return MT <= 1 ? 8 : MT <= 2 ? 6 : MT <= 4 ? 4 : 2;
 }
 
-// K loop over NSTEPS steps with a register prefetch ring: fully unrolled for
-// short K ranges (exact load counting), a rolled ring otherwise (the long
-// unroll would spill).
+// K loop over NSTEPS steps with a register prefetch ring, fully unrolled
+// (exact load counting).
 template <int MT, int NSTEPS>
 __device__ __forceinline__ void route_kloop(const RouteLoader<MT>& L, f32x16 (&acc)[MT]) {
+  static_assert(NSTEPS <= 16, "a longer unroll would spill");
   constexpr int D = route_depth<MT>() < NSTEPS ? route_depth<MT>() : NSTEPS;
   RStage<MT> st[D];
 #pragma unroll
@@ -139,25 +145,11 @@ __device__ __forceinline__ void route_kloop(const RouteLoader<MT>& L, f32x16 (&a
   // free, the scheduler sinks them next to their use and only about one
   // step stays in flight
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (NSTEPS <= 16) {
 #pragma unroll
-    for (int s = 0; s < NSTEPS; ++s) {
-      route_mma<MT>(st[s % D], acc);
-      if (s + D < NSTEPS) L.load(st[s % D], s + D);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  } else {
-    for (int s0 = 0; s0 < NSTEPS; s0 += D) {
-#pragma unroll
-      for (int q = 0; q < D; ++q) {
-        const int s = s0 + q;
-        if (s < NSTEPS) {
-          route_mma<MT>(st[q], acc);
-          if (s + D < NSTEPS) L.load(st[q], s + D);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+  for (int s = 0; s < NSTEPS; ++s) {
+    route_mma<MT>(st[s % D], acc);
+    if (s + D < NSTEPS) L.load(st[s % D], s + D);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -244,77 +236,184 @@ __device__ __forceinline__ void lanes_topk(const float* lg, int e_stride, int E,
 }
 
 constexpr int kTopkLanes = 8;   // lanes per token in the top-k
+constexpr int kRouteTwoTileBlocks = 256;   // blocks of 64 tokens that fill the chip
 
 // ---------------------------------------------------------------- many tokens
-template <int MT, int WK>
-__global__ __launch_bounds__(WK * 64) void route_kernel(const uint16_t* __restrict__ x,
-                                                        const float* __restrict__ Wr,
-                                                        const float* __restrict__ br, int T, int E,
-                                                        int k, int32_t* __restrict__ ids,
-                                                        float* __restrict__ wts,
-                                                        float* __restrict__ logits,
-                                                        int32_t* __restrict__ block_hist) {
-  constexpr int KW = kH / WK;      // K range of one wave
-  constexpr int KSTEPS = KW / 16;  // MFMA steps of one wave
-  constexpr int LDR = 33;          // padded row of the reduction buffer
-  static_assert(KW % 16 == 0, "K split must be a multiple of 16");
-  extern __shared__ float red[];   // [MT * 32][LDR]
+// The fp32 router weights are split once per call into their three bf16
+// pieces, stored in MFMA operand order: fragment (s, mt, p) is 64 lanes x 8
+// bf16 (1 KiB), lane (n, hh) holding piece p (lo, mid, hi) of
+// Wr[32 mt + n][16 s + 8 hh .. + 7]; experts past E are zero. The tile
+// kernel then streams whole fragments (one coalesced 1 KiB load each) with no
+// arithmetic besides the MFMAs.
+size_t route_split_bytes(int E) { return (size_t)kRouteSteps * ((E + 31) / 32) * 3 * 1024; }
+
+__global__ __launch_bounds__(256) void route_split_kernel(const float* __restrict__ Wr, int E,
+                                                          int MT, uint4* __restrict__ Wp) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= kRouteSteps * MT * 64) return;
+  const int lane = idx & 63;
+  const int mt = (idx >> 6) % MT;
+  const int s = (idx >> 6) / MT;
+  const int e = mt * 32 + (lane & 31);
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+  if (e < E) {
+    const float* src = Wr + (size_t)e * kH + 16 * s + 8 * (lane >> 5);
+    a = *reinterpret_cast<const float4*>(src);
+    b = *reinterpret_cast<const float4*>(src + 4);
+  }
+  bf16x8 fh, fm, fl;
+  split_frag(a, b, fh, fm, fl);
+  uint4* dst = Wp + (size_t)((s * MT + mt) * 3) * 64 + lane;
+  dst[0] = __builtin_bit_cast(uint4, fl);
+  dst[64] = __builtin_bit_cast(uint4, fm);
+  dst[128] = __builtin_bit_cast(uint4, fh);
+}
+
+// Register-tiled router: a block of KS waves owns 32*NTW tokens; wave w
+// computes all 32*MT experts of those tokens over the K range
+// [w*2880/KS, (w+1)*2880/KS), holding NTW token tiles so that every weight
+// fragment it loads feeds NTW MFMAs. The K loop is fully unrolled over a
+// D-deep register ring (exact load accounting). The KS partial tiles meet in
+// LDS and are added in wave order, then the bias, the top k and the routed-slot
+// histograms of the block's 32-token groups.
+template <int MT, int NTW, int KS>
+struct RouteTileCfg {
+  static constexpr int kSteps = kRouteSteps / KS;   // K steps of one wave
+  static constexpr int kTB = 32 * NTW;              // tokens per block
+  // partial-tile row: rows 4 apart (the two lane halves) land 32 banks apart
+  // when it fits the LDS, else 16
+  static constexpr int kLdr = kTB + (MT > 4 ? 4 : 8);
+  static constexpr int kStageRegs = 4 * NTW + 12 * MT;
+  // ring depth from the register budget: up to 224 VGPRs beside the
+  // accumulators (which the compiler moves to AGPRs) at one wave per SIMD,
+  // 168 in all at the three waves per SIMD of 12 K splits
+  static constexpr int kRingRegs = KS > 4 ? 168 - 16 * NTW * MT - 32 : 224;
+  static constexpr int kDepth = kRingRegs / kStageRegs > 8 ? 8
+                                : kRingRegs / kStageRegs < 2 ? 2 : kRingRegs / kStageRegs;
+  static constexpr int kRedFloats = KS * MT * 32 * kLdr;
+  static_assert(kSteps * KS == kRouteSteps, "the K split must divide the K steps");
+  static_assert(kRedFloats * 4 + kTB * kMaxTopK * 4 <= 160 * 1024, "LDS");
+};
+
+template <int MT, int NTW>
+struct RTStage {
+  uint4 xv[NTW];
+  uint4 f[MT][3];
+};
+
+template <int MT, int NTW, int KS>
+__global__ __launch_bounds__(KS * 64) void route_tile_kernel(
+    const uint16_t* __restrict__ x, const uint4* __restrict__ Wp, const float* __restrict__ br,
+    int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wts,
+    float* __restrict__ logits, int32_t* __restrict__ block_hist) {
+  using C = RouteTileCfg<MT, NTW, KS>;
+  constexpr int D = C::kDepth;
+  constexpr int LDR = C::kLdr;
+  constexpr int TB = C::kTB;
+  __shared__ float red[C::kRedFloats];           // [KS][MT*32][LDR] partial logits
+  __shared__ int32_t sel[TB * kMaxTopK];         // the block's chosen experts
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int tok0 = blockIdx.x * 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;
   const int hh = lane >> 5;
+  const int tok0 = blockIdx.x * TB;
 
-  f32x16 acc[MT];
+  // padded tokens read a clamped valid row; their results are never used
+  const uint16_t* xr[NTW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
-  RouteLoader<MT> L;
-  L.init(x, Wr, T, E, tok0 + n, wave * KW, lane);
-  route_kloop<MT, KSTEPS>(L, acc);
+  for (int tw = 0; tw < NTW; ++tw)
+    xr[tw] = x + (size_t)min(tok0 + 32 * tw + n, T - 1) * kH + wave * (C::kSteps * 16) + 8 * hh;
+  const uint4* wp = Wp + (size_t)wave * C::kSteps * MT * 3 * 64 + lane;
 
-  // Fixed-order split-K reduction: red[e][token] = sum over waves 0..WK-1.
-  // 32x32 result layout: lane holds column n (token), rows 8q + 4hh + j.
-  for (int w = 0; w < WK; ++w) {
-    if (wave == w) {
+  f32x16 acc[NTW][MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+  for (int tw = 0; tw < NTW; ++tw)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float* p = &red[(mt * 32 + 8 * q + 4 * hh + j) * LDR + n];
-            *p = (w == 0) ? acc[mt][4 * q + j] : (*p + acc[mt][4 * q + j]);
-          }
-    }
-    __syncthreads();
-  }
+    for (int mt = 0; mt < MT; ++mt) acc[tw][mt] = f32x16{};
 
-  // bias, optional logits output
-  for (int i = threadIdx.x; i < 32 * E; i += WK * 64) {
-    const int e = i / 32, tt = i % 32;
-    const float v = red[e * LDR + tt] + br[e];
-    red[e * LDR + tt] = v;
-    if (logits && tok0 + tt < T) logits[(size_t)(tok0 + tt) * E + e] = v;
+  RTStage<MT, NTW> st[D];
+  auto load = [&](RTStage<MT, NTW>& S, int s) __attribute__((always_inline)) {
+    // opaque step offsets: each step computes its own addresses instead of
+    // the compiler keeping every step's pointers live
+    int xo = 16 * s, wo = s * MT * 3 * 64;
+    asm volatile("" : "+s"(xo), "+s"(wo));
+#pragma unroll
+    for (int tw = 0; tw < NTW; ++tw) S.xv[tw] = *reinterpret_cast<const uint4*>(xr[tw] + xo);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) S.f[mt][p] = wp[wo + (mt * 3 + p) * 64];
+  };
+  static_for<D>([&](auto Q) __attribute__((always_inline)) { load(st[Q], Q); });
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<C::kSteps>([&](auto S) __attribute__((always_inline)) {
+    constexpr int s = S;
+    RTStage<MT, NTW>& cur = st[s % D];
+    // pieces lo, mid, hi in turn; the NTW*MT accumulators in between keep
+    // dependent MFMAs apart
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int tw = 0; tw < NTW; ++tw)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[tw][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              u4_as_bf16x8(cur.f[mt][p]), u4_as_bf16x8(cur.xv[tw]), acc[tw][mt], 0, 0, 0);
+    if constexpr (s + D < C::kSteps) load(cur, s + D);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+
+  // partial tiles: red[wave][e][t]; 32x32 result layout: lane holds column n
+  // (token), rows 8q + 4hh + j (experts)
+  float* mine = red + (size_t)wave * MT * 32 * LDR;
+#pragma unroll
+  for (int tw = 0; tw < NTW; ++tw)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          mine[(mt * 32 + 8 * q + 4 * hh + j) * LDR + 32 * tw + n] = acc[tw][mt][4 * q + j];
+  __syncthreads();
+  // logits = partials added in wave order, then the bias; into slice 0
+  for (int i = threadIdx.x; i < E * TB; i += KS * 64) {
+    const int e = i / TB, t = i - (i / TB) * TB;
+    float v = red[e * LDR + t];
+#pragma unroll
+    for (int w = 1; w < KS; ++w) v += red[(size_t)w * MT * 32 * LDR + e * LDR + t];
+    v += br[e];
+    red[e * LDR + t] = v;
+    if (logits && tok0 + t < T) logits[(size_t)(tok0 + t) * E + e] = v;
   }
   __syncthreads();
-  // top-k: 8 lanes per token, the first 256 threads cover the 32 tokens
-  if (threadIdx.x < 32 * kTopkLanes) {
-    const int tt = threadIdx.x / kTopkLanes;
-    const int t = tok0 + tt;
-    lanes_topk<kTopkLanes>(red + tt, LDR, E, k, t < T, ids + (size_t)t * k, wts + (size_t)t * k,
-                           nullptr);
+  // top k: kTopkLanes lanes per token (the count of such lanes is a multiple
+  // of 64, so every wave takes part in a round as a whole)
+  for (int base = 0; base < TB * kTopkLanes; base += KS * 64) {
+    const int i = base + threadIdx.x;
+    if (i < TB * kTopkLanes) {
+      const int tt = i / kTopkLanes;
+      const int t = tok0 + tt;
+      lanes_topk<kTopkLanes>(red + tt, LDR, E, k, t < T, ids + (size_t)t * k, wts + (size_t)t * k,
+                             sel + tt * k);
+    }
   }
   if (block_hist) {
-    // expert histogram of this block's routed slots, for the parallel permutation
-    int* hist = reinterpret_cast<int*>(red);   // the logits tile is no longer needed
+    // expert histograms of the block's 32-token groups, for the parallel
+    // permutation (the partial tiles are no longer needed)
+    int* hist = reinterpret_cast<int*>(red);   // [NTW][E]
+    __syncthreads();   // the top k has read its logits and written sel
+    for (int i = threadIdx.x; i < NTW * E; i += KS * 64) hist[i] = 0;
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += WK * 64) hist[e] = 0;
+    const int nslots = (min(T, tok0 + TB) - tok0) * k;
+    for (int i = threadIdx.x; i < nslots; i += KS * 64) atomicAdd(&hist[(i / (32 * k)) * E + sel[i]], 1);
     __syncthreads();
-    const int nslots = (min(T, tok0 + 32) - tok0) * k;
-    for (int i = threadIdx.x; i < nslots; i += WK * 64) atomicAdd(&hist[ids[(size_t)tok0 * k + i]], 1);
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += WK * 64) block_hist[(size_t)blockIdx.x * E + e] = hist[e];
+    const int groups = (T + 31) / 32;
+    for (int i = threadIdx.x; i < NTW * E; i += KS * 64) {
+      const int g = blockIdx.x * NTW + i / E;
+      if (g < groups) block_hist[(size_t)g * E + i % E] = hist[i];
+    }
   }
 }
 
@@ -500,27 +599,33 @@ static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const floa
     }
     return hipGetLastError();
   }
-  const int blocks = (T + 31) / 32;
-  const size_t lds = (size_t)MT * 32 * 33 * sizeof(float);
-  static_assert(32 * 33 >= kMaxExperts, "the reduction tile doubles as the histogram");
-  int32_t* hist = reinterpret_cast<int32_t*>(scratch);   // [blocks][E] routed-slot histograms
-  // 12 waves split K when few blocks would run; only for one expert tile,
-  // where the 768-thread register budget holds the prefetch ring.
-  if constexpr (MT == 1) {
-    if (blocks < 256) {
-      hipLaunchKernelGGL((route_kernel<1, 12>), dim3(blocks), dim3(12 * 64), lds, s, x, Wr, br, T, E,
-                         k, ids, w, logits, counts ? hist : nullptr);
-    } else {
-      hipLaunchKernelGGL((route_kernel<1, 4>), dim3(blocks), dim3(4 * 64), lds, s, x, Wr, br, T, E,
-                         k, ids, w, logits, counts ? hist : nullptr);
-    }
+  // split weights first (16-byte aligned: a multiple of 1 KiB), then the histograms
+  uint4* wp = reinterpret_cast<uint4*>(scratch);
+  int32_t* hist = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(scratch) + route_split_bytes(E));
+  hipLaunchKernelGGL(route_split_kernel, dim3((kRouteSteps * MT * 64 + 255) / 256), dim3(256), 0, s,
+                     Wr, E, MT, wp);
+  int32_t* bh = counts ? hist : nullptr;
+  // one or two token tiles per wave (two halve the weight traffic per token
+  // once the token count alone keeps every CU busy); more K splits for few
+  // expert tiles, whose waves have little work per step
+  if constexpr (MT <= 2) {
+    hipLaunchKernelGGL((route_tile_kernel<MT, 1, 12>), dim3((T + 31) / 32), dim3(12 * 64), 0, s, x,
+                       wp, br, T, E, k, ids, w, logits, bh);
+  } else if constexpr (MT <= 4) {
+    if ((T + 63) / 64 >= kRouteTwoTileBlocks)
+      hipLaunchKernelGGL((route_tile_kernel<MT, 2, 4>), dim3((T + 63) / 64), dim3(4 * 64), 0, s, x,
+                         wp, br, T, E, k, ids, w, logits, bh);
+    else
+      hipLaunchKernelGGL((route_tile_kernel<MT, 1, 4>), dim3((T + 31) / 32), dim3(4 * 64), 0, s, x,
+                         wp, br, T, E, k, ids, w, logits, bh);
   } else {
-    hipLaunchKernelGGL((route_kernel<MT, 4>), dim3(blocks), dim3(4 * 64), lds, s, x, Wr, br, T, E, k,
-                       ids, w, logits, counts ? hist : nullptr);
+    hipLaunchKernelGGL((route_tile_kernel<MT, 1, 4>), dim3((T + 31) / 32), dim3(4 * 64), 0, s, x,
+                       wp, br, T, E, k, ids, w, logits, bh);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !counts) return err;
-  return launch_permute_blocks(ids, T * k, E, hist, blocks, 32 * k, counts, offsets, sorted_rows, s);
+  return launch_permute_blocks(ids, T * k, E, hist, (T + 31) / 32, 32 * k, counts, offsets,
+                               sorted_rows, s);
 }
 
 hipError_t launch_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,

@@ -65,8 +65,14 @@ def test_pack_weights_layout(E, N):
 
 
 # ---------------------------------------------------------------- route
+# few-token schedule up to T = 128 (T*E <= 4096); above, the register-tiled
+# kernel: 12 K splits for E <= 64 (1000, 64), one token tile per wave for
+# E = 96 (130, ragged expert tile), 128 (257), 160 (200) and 256 (300), and
+# two per wave from 256 blocks of 64 tokens on (16384; 16411 with a ragged
+# last block and E = 100)
 ROUTE_CASES = [(1, 4, 1), (2, 32, 4), (3, 32, 4), (16, 32, 4), (17, 128, 4), (64, 32, 4),
-               (100, 7, 3), (33, 256, 8), (257, 128, 4), (4096, 32, 4), (16384, 128, 4)]
+               (100, 7, 3), (33, 256, 8), (130, 96, 6), (1000, 64, 4), (200, 160, 4),
+               (257, 128, 4), (300, 256, 8), (4096, 32, 4), (16384, 128, 4), (16411, 100, 4)]
 
 
 @pytest.mark.parametrize("T,E,k", ROUTE_CASES)
@@ -101,6 +107,34 @@ def test_route_deterministic():
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+def test_forward_ragged_two_tile_router():
+    """T = 16411 tokens, E = 100: the router's 64-token blocks (a ragged last
+    block, a padded expert tile) count the routed slots of each 32-token group,
+    and the layer's permutation is built from those counts. Every row of the
+    one-call layer against the separate calls (whose permutation counts the
+    slots itself), and the first and last routed token of every expert
+    against the oracle."""
+    T, E, k = 16411, 100, 4
+    say(f"forward T={T} E={E} k={k}: router histograms")
+    inp = make_layer_inputs(T, E, k, seed=16411)
+    d = to_device(inp)
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+    out = moe.forward(d["x"], d["Wr"], d["br"], *weights_args(d), k=k)
+    counts, offsets, rows = moe.permute(ids, E)
+    y = moe.expert_ffn(d["x"], offsets, rows, *weights_args(d), k=k)
+    out_unfused = moe.combine(y, w)
+    torch.cuda.synchronize()
+    ids_h = np_(ids)
+    logits = oracle.router_logits(inp["x"], inp["Wr"], inp["br"])
+    check_routing(ids_h, np_(w), logits, k)
+    m_all = out_metrics(np_(out), np_(out_unfused).astype(np.float64))
+    assert m_all["max_err_over_rms"] < 1e-4, m_all
+    sample = np.unique(np.concatenate([[0, T - 1], expert_edge_tokens(ids_h, E)]))
+    ref = oracle.forward(inp, k, tokens=sample, ids_override=ids_h)
+    m = assert_out_close(np_(out)[sample], ref["out"], "T=16411 E=100")
+    say(f"  {sample.size} edge tokens {m}; fused vs unfused {m_all}")
 
 
 # ---------------------------------------------------------------- permute
