@@ -245,8 +245,15 @@ constexpr int kRouteTwoTileBlocks = 256;   // blocks of 64 tokens that fill the 
 // Wr[32 mt + n][16 s + 8 hh .. + 7]; experts past E are zero. The tile
 // kernel then streams whole fragments (one coalesced 1 KiB load each) with no
 // arithmetic besides the MFMAs.
-size_t route_split_bytes(int E) { return (size_t)kRouteSteps * ((E + 31) / 32) * 3 * 1024; }
+// Expert tiles of the split weights: E rounded up to 32, and for the
+// expert-tiled kernel further to a whole number of tiles per wave.
+constexpr int route_tiles_padded(int MT) { return MT <= 4 ? MT : MT <= 6 ? 6 : 8; }
 
+size_t route_split_bytes(int E) {
+  return (size_t)kRouteSteps * route_tiles_padded((E + 31) / 32) * 3 * 1024;
+}
+
+// MT = padded expert tiles of the layout; tiles past E are zero
 __global__ __launch_bounds__(256) void route_split_kernel(const float* __restrict__ Wr, int E,
                                                           int MT, uint4* __restrict__ Wp) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(256) void route_split_kernel(const float* __restric
   dst[128] = __builtin_bit_cast(uint4, fh);
 }
 
-// Register-tiled router: a block of KS waves owns 32*NTW tokens; wave w
+// K-split router (E <= 64): a block of KS waves owns 32*NTW tokens; wave w
 // computes all 32*MT experts of those tokens over the K range
 // [w*2880/KS, (w+1)*2880/KS), holding NTW token tiles so that every weight
 // fragment it loads feeds NTW MFMAs. The K loop is fully unrolled over a
@@ -302,7 +309,7 @@ struct RTStage {
 };
 
 template <int MT, int NTW, int KS>
-__global__ __launch_bounds__(KS * 64) void route_tile_kernel(
+__global__ __launch_bounds__(KS * 64) void route_ksplit_kernel(
     const uint16_t* __restrict__ x, const uint4* __restrict__ Wp, const float* __restrict__ br,
     int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wts,
     float* __restrict__ logits, int32_t* __restrict__ block_hist) {
@@ -411,6 +418,207 @@ __global__ __launch_bounds__(KS * 64) void route_tile_kernel(
     __syncthreads();
     const int groups = (T + 31) / 32;
     for (int i = threadIdx.x; i < NTW * E; i += KS * 64) {
+      const int g = blockIdx.x * NTW + i / E;
+      if (g < groups) block_hist[(size_t)g * E + i % E] = hist[i];
+    }
+  }
+}
+
+// Expert-tiled router (E > 64): a block of W waves owns 32*NTW tokens; wave
+// w computes expert tiles [w*MTW, (w+1)*MTW) of them over all of K, so no
+// partial sums cross waves and each logit is one fixed-order accumulation
+// plus the bias. The block's activation rows pass through a two-slot LDS
+// ring of 64-K groups (whole 128-byte lines per row, loaded two groups ahead
+// into registers and shared by all waves); each wave streams only its own
+// tiles' weight fragments through a register ring. One barrier per group.
+template <int MTW, int W, int NTW>
+struct RouteWideCfg {
+  static constexpr int kTB = 32 * NTW;               // tokens per block
+  static constexpr int kGroups = kH / 64;            // 45 groups of 4 K steps
+  static constexpr int kPieces = kTB * 8;            // 16-byte pieces of a group
+  static constexpr int kXLoads = (kPieces + W * 64 - 1) / (W * 64);
+  static constexpr int kMTP = W * MTW;               // padded expert tiles
+  static constexpr int kLdr = kTB + 8;               // logit row: lane halves 32 banks apart
+  static constexpr int kStageRegs = 12 * MTW;
+  static constexpr int kDepth = 96 / kStageRegs > 8 ? 8 : 96 / kStageRegs;
+  static_assert(kGroups * 64 == kH, "groups must tile K");
+};
+
+// LDS byte offset of 16-byte piece p of row r in a group slot (rows of 128
+// bytes; pieces XOR-swizzled by r/2 so that a 32-row fragment read is free of
+// bank conflicts)
+__device__ __forceinline__ int route_xs_off(int r, int p) { return r * 128 + ((p ^ ((r >> 1) & 7)) << 4); }
+
+template <int MTW, int W, int NTW>
+__global__ __launch_bounds__(W * 64) void route_tile_kernel(
+    const uint16_t* __restrict__ x, const uint4* __restrict__ Wp, const float* __restrict__ br,
+    int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wts,
+    float* __restrict__ logits, int32_t* __restrict__ block_hist) {
+  using C = RouteWideCfg<MTW, W, NTW>;
+  constexpr int D = C::kDepth;
+  constexpr int TB = C::kTB;
+  constexpr int LDR = C::kLdr;
+  constexpr int MTP = C::kMTP;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][TB * 128];   // activation group ring
+  __shared__ float lg[MTP * 32 * LDR];                               // [expert][token] logits
+  __shared__ int32_t sel[TB * kMaxTopK];                             // the block's chosen experts
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int tok0 = blockIdx.x * TB;
+
+  // activation pieces this thread stages: piece q = tid + i*W*64 of a group,
+  // row q/8 (token, clamped to a valid row: padded tokens' results are never
+  // used), 16-byte piece q%8; threads past the last piece load a valid
+  // duplicate and skip the store
+  const uint16_t* xsrc[C::kXLoads];
+  int xdst[C::kXLoads];
+#pragma unroll
+  for (int i = 0; i < C::kXLoads; ++i) {
+    const int q = tid + i * W * 64;
+    const int qc = min(q, C::kPieces - 1);
+    const int r = qc >> 3, p = qc & 7;
+    xsrc[i] = x + (size_t)min(tok0 + r, T - 1) * kH + 8 * p;
+    xdst[i] = q < C::kPieces ? route_xs_off(r, p) : -1;
+  }
+  // (compile-time indices throughout, so that the staging registers stay
+  // registers and are never placed in memory)
+  u32x4 xra[C::kXLoads], xrb[C::kXLoads];   // staging registers of alternate groups
+  auto load_group = [&](u32x4 (&R)[C::kXLoads], int g) __attribute__((always_inline)) {
+    int go = 64 * g;
+    asm volatile("" : "+s"(go));
+    static_for<C::kXLoads>([&](auto I) __attribute__((always_inline)) {
+      R[I] = *reinterpret_cast<const u32x4*>(xsrc[I] + go);
+    });
+  };
+  auto store_group = [&](const u32x4 (&R)[C::kXLoads], int slot) __attribute__((always_inline)) {
+    static_for<C::kXLoads>([&](auto I) __attribute__((always_inline)) {
+      if (xdst[I] >= 0) *reinterpret_cast<u32x4*>(&xs[slot][xdst[I]]) = R[I];
+    });
+  };
+  // fragment of token tile tw, K step j of a group: row 32 tw + n, piece 2j + hh
+  auto read_frags = [&](uint4 (&F)[NTW], int slot, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tw = 0; tw < NTW; ++tw)
+      F[tw] = *reinterpret_cast<const uint4*>(&xs[slot][route_xs_off(32 * tw + n, 2 * j + hh)]);
+  };
+
+  // this wave's weight fragments: tiles wave*MTW .. + MTW of every step
+  const uint4* wp = Wp + (size_t)wave * MTW * 3 * 64 + lane;
+  uint4 ring[D][MTW][3];
+  auto load_w = [&](uint4 (&S)[MTW][3], int s) __attribute__((always_inline)) {
+    int wo = s * MTP * 3 * 64;
+    asm volatile("" : "+s"(wo));
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) S[m][p] = wp[wo + (m * 3 + p) * 64];
+  };
+
+  f32x16 acc[NTW][MTW];
+#pragma unroll
+  for (int tw = 0; tw < NTW; ++tw)
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) acc[tw][m] = f32x16{};
+
+  // group barrier: this thread's LDS writes done, then the workgroup barrier
+  // (no wait on the weight loads in flight)
+  auto group_sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");        // no LDS access moves across it
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: groups 0 and 1 into registers, group 0 into slot 0, group 2
+  // into registers; the weight ring's first D steps
+  load_group(xra, 0);
+  load_group(xrb, 1);
+  static_for<D>([&](auto Q) __attribute__((always_inline)) { load_w(ring[Q], Q); });
+  store_group(xra, 0);
+  load_group(xra, 2);
+  group_sync();
+  uint4 xf[2][NTW];
+  read_frags(xf[0], 0, 0);
+
+  static_for<C::kGroups>([&](auto G) __attribute__((always_inline)) {
+    constexpr int g = G;
+    // group g+1 into the other slot (its last readers passed the previous
+    // barrier), and its registers refilled with group g+3
+    auto& xr = [&]() -> auto& { if constexpr ((g + 1) & 1) return xrb; else return xra; }();
+    if constexpr (g + 1 < C::kGroups) store_group(xr, (g + 1) & 1);
+    if constexpr (g + 3 < C::kGroups) load_group(xr, g + 3);
+    static_for<4>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = J;
+      constexpr int s = 4 * g + j;
+      const uint4 (&cur)[NTW] = xf[s & 1];
+      // pieces lo, mid, hi in turn; the NTW*MTW accumulators in between
+      // keep dependent MFMAs apart
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int tw = 0; tw < NTW; ++tw)
+#pragma unroll
+          for (int m = 0; m < MTW; ++m)
+            acc[tw][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                u4_as_bf16x8(ring[s % D][m][p]), u4_as_bf16x8(cur[tw]), acc[tw][m], 0, 0, 0);
+      if constexpr (s + D < kRouteSteps) load_w(ring[s % D], s + D);
+      if constexpr (j < 3) {
+        read_frags(xf[(s + 1) & 1], g & 1, j + 1);
+      } else if constexpr (g + 1 < C::kGroups) {
+        group_sync();   // group g+1 is in its slot; everyone is done with slot g&1
+        read_frags(xf[(s + 1) & 1], (g + 1) & 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
+
+  // logits (+ bias) into LDS; 32x32 result layout: lane holds column n
+  // (token), rows 8q + 4hh + j (experts)
+#pragma unroll
+  for (int tw = 0; tw < NTW; ++tw)
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 32 * (wave * MTW + m) + 8 * q + 4 * hh + j;
+          lg[e * LDR + 32 * tw + n] = acc[tw][m][4 * q + j] + (e < E ? br[e] : 0.f);
+        }
+  __syncthreads();
+  if (logits) {
+    for (int i = tid; i < E * TB; i += W * 64) {
+      const int e = i / TB, t = i - (i / TB) * TB;
+      if (tok0 + t < T) logits[(size_t)(tok0 + t) * E + e] = lg[e * LDR + t];
+    }
+  }
+  // top k: kTopkLanes lanes per token (a multiple of 64 lanes per round, so
+  // every wave takes part in a round as a whole)
+  for (int base = 0; base < TB * kTopkLanes; base += W * 64) {
+    const int i = base + tid;
+    if (i < TB * kTopkLanes) {
+      const int tt = i / kTopkLanes;
+      const int t = tok0 + tt;
+      lanes_topk<kTopkLanes>(lg + tt, LDR, E, k, t < T, ids + (size_t)t * k, wts + (size_t)t * k,
+                             sel + tt * k);
+    }
+  }
+  if (block_hist) {
+    // expert histograms of the block's 32-token groups, for the parallel
+    // permutation (the logits are no longer needed)
+    int* hist = reinterpret_cast<int*>(lg);   // [NTW][E]
+    __syncthreads();   // the top k has read its logits and written sel
+    for (int i = tid; i < NTW * E; i += W * 64) hist[i] = 0;
+    __syncthreads();
+    const int nslots = (min(T, tok0 + TB) - tok0) * k;
+    for (int i = tid; i < nslots; i += W * 64) atomicAdd(&hist[(i / (32 * k)) * E + sel[i]], 1);
+    __syncthreads();
+    const int groups = (T + 31) / 32;
+    for (int i = tid; i < NTW * E; i += W * 64) {
       const int g = blockIdx.x * NTW + i / E;
       if (g < groups) block_hist[(size_t)g * E + i % E] = hist[i];
     }
@@ -600,27 +808,27 @@ static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const floa
     return hipGetLastError();
   }
   // split weights first (16-byte aligned: a multiple of 1 KiB), then the histograms
+  constexpr int MTP = route_tiles_padded(MT);
   uint4* wp = reinterpret_cast<uint4*>(scratch);
   int32_t* hist = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(scratch) + route_split_bytes(E));
-  hipLaunchKernelGGL(route_split_kernel, dim3((kRouteSteps * MT * 64 + 255) / 256), dim3(256), 0, s,
-                     Wr, E, MT, wp);
+  hipLaunchKernelGGL(route_split_kernel, dim3((kRouteSteps * MTP * 64 + 255) / 256), dim3(256), 0, s,
+                     Wr, E, MTP, wp);
   int32_t* bh = counts ? hist : nullptr;
-  // one or two token tiles per wave (two halve the weight traffic per token
-  // once the token count alone keeps every CU busy); more K splits for few
-  // expert tiles, whose waves have little work per step
   if constexpr (MT <= 2) {
-    hipLaunchKernelGGL((route_tile_kernel<MT, 1, 12>), dim3((T + 31) / 32), dim3(12 * 64), 0, s, x,
+    // few expert tiles: waves split K (little work per wave and step)
+    hipLaunchKernelGGL((route_ksplit_kernel<MT, 1, 12>), dim3((T + 31) / 32), dim3(12 * 64), 0, s, x,
                        wp, br, T, E, k, ids, w, logits, bh);
-  } else if constexpr (MT <= 4) {
+  } else {
+    // a wave per one or two expert tiles; two token tiles per wave (half the
+    // weight traffic per token) once 64-token blocks alone fill the chip
+    constexpr int MTW = MT <= 4 ? 1 : 2;
+    constexpr int WV = MTP / MTW;
     if ((T + 63) / 64 >= kRouteTwoTileBlocks)
-      hipLaunchKernelGGL((route_tile_kernel<MT, 2, 4>), dim3((T + 63) / 64), dim3(4 * 64), 0, s, x,
+      hipLaunchKernelGGL((route_tile_kernel<MTW, WV, 2>), dim3((T + 63) / 64), dim3(WV * 64), 0, s, x,
                          wp, br, T, E, k, ids, w, logits, bh);
     else
-      hipLaunchKernelGGL((route_tile_kernel<MT, 1, 4>), dim3((T + 31) / 32), dim3(4 * 64), 0, s, x,
+      hipLaunchKernelGGL((route_tile_kernel<MTW, WV, 1>), dim3((T + 31) / 32), dim3(WV * 64), 0, s, x,
                          wp, br, T, E, k, ids, w, logits, bh);
-  } else {
-    hipLaunchKernelGGL((route_tile_kernel<MT, 1, 4>), dim3((T + 31) / 32), dim3(4 * 64), 0, s, x,
-                       wp, br, T, E, k, ids, w, logits, bh);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !counts) return err;
