@@ -8,8 +8,58 @@
 
 namespace moe {
 
-constexpr int kNormRowVec = kH / 8;                  // 360 16-byte vectors per row
-constexpr int kNormPerLane = (kNormRowVec + 63) / 64;   // 6
+// One wave per bf16 row of kH values, lane l holding 16-byte vectors l,
+// l + 64, ...
+constexpr int kNormRowVec = kH / 8;                      // 360 16-byte vectors per row
+constexpr int kNormPerLane = (kNormRowVec + 63) / 64;    // 6
+
+// the lane's raw vectors of a row (zero past the row's end)
+__device__ __forceinline__ void norm_load_raw(const uint16_t* row, int lane,
+                                              uint4 (&d)[kNormPerLane]) {
+  const uint4* xr = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+  for (int j = 0; j < kNormPerLane; ++j) {
+    const int i = lane + 64 * j;
+    d[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (i < kNormRowVec) d[j] = xr[i];
+  }
+}
+
+// 1 / sqrt(mean(x^2) + eps) of the row from the lane's raw vectors: the
+// squares are summed per lane by bf16 dot-2 instructions (fp32 accumulate)
+// into four partial sums, one per dword position, added in a fixed order,
+// then a butterfly over the 64 lanes adds the lanes' sums; every lane gets
+// the result.
+__device__ __forceinline__ float norm_inv_rms(const uint4 (&d)[kNormPerLane], float eps) {
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kNormPerLane; ++j) {
+    const uint32_t dw[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x2 v = __builtin_bit_cast(bf16x2, dw[q]);
+      ss[q] = __builtin_amdgcn_fdot2_f32_bf16(v, v, ss[q], false);
+    }
+  }
+  float t = (ss[0] + ss[1]) + (ss[2] + ss[3]);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) t += __shfl_xor(t, m, 64);
+  return 1.0f / sqrtf(t / (float)kH + eps);
+}
+
+// bf16(x * inv * scale) of 8 consecutive bf16 values (two per dword) and their
+// 8 scale values
+__device__ __forceinline__ uint4 norm_apply8(const uint4 d, float inv, const float4 s0,
+                                             const float4 s1) {
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+  const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = f32_to_bf16_bits(bf16_bits_to_f32(dw[q] & 0xFFFFu) * inv * s[2 * q]) |
+           (f32_to_bf16_bits(bf16_bits_to_f32(dw[q] >> 16) * inv * s[2 * q + 1]) << 16);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
 
 // One wave per row, four rows per 256-thread block. The sum of squares is
 // reduced in a fixed order (per lane, then a butterfly), so results are
@@ -20,40 +70,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= T) return;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + row * kH);
-  float v[kNormPerLane][8];
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < kNormPerLane; ++j) {
-    const int i = lane + 64 * j;
-    uint4 d = make_uint4(0u, 0u, 0u, 0u);
-    if (i < kNormRowVec) d = xr[i];
-    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[j][2 * q] = bf16_bits_to_f32(dw[q] & 0xFFFFu);
-      v[j][2 * q + 1] = bf16_bits_to_f32(dw[q] >> 16);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) ss = fmaf(v[j][q], v[j][q], ss);
-  }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) ss += __shfl_xor(ss, d, 64);
-  const float inv = 1.0f / sqrtf(ss / (float)kH + eps);
+  uint4 d[kNormPerLane];
+  norm_load_raw(x + row * kH, lane, d);
+  const float inv = norm_inv_rms(d, eps);
   uint4* tr = reinterpret_cast<uint4*>(t + row * kH);
   const float4* sc = reinterpret_cast<const float4*>(scale);
 #pragma unroll
   for (int j = 0; j < kNormPerLane; ++j) {
     const int i = lane + 64 * j;
     if (i >= kNormRowVec) break;
-    const float4 s0 = sc[2 * i], s1 = sc[2 * i + 1];
-    const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      o[q] = f32_to_bf16_bits(v[j][2 * q] * inv * s[2 * q]) |
-             (f32_to_bf16_bits(v[j][2 * q + 1] * inv * s[2 * q + 1]) << 16);
-    tr[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    tr[i] = norm_apply8(d[j], inv, sc[2 * i], sc[2 * i + 1]);
   }
 }
 

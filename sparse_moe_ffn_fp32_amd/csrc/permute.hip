@@ -186,11 +186,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   for (int j = 0; j < k; ++j) {
     const float wt = w[(size_t)t * k + j];
-    const float4 v = reinterpret_cast<const float4*>(y)[((size_t)t * k + j) * C4 + c];
-    acc.x += wt * v.x;
-    acc.y += wt * v.y;
-    acc.z += wt * v.z;
-    acc.w += wt * v.w;
+    // y is read once: non-temporal loads keep it from evicting the caches
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y) + ((size_t)t * k + j) * C4 + c);
+    acc.x += wt * v[0];
+    acc.y += wt * v[1];
+    acc.z += wt * v[2];
+    acc.w += wt * v[3];
   }
   reinterpret_cast<float4*>(out)[(size_t)t * C4 + c] = acc;
 }

@@ -65,7 +65,10 @@ def test_rmsnorm(T, eps):
     assert frac < 1e-2
 
 
-BLOCK_CASES = [(16, 32, 4), (130, 2, 2), (256, 8, 4), (300, 4, 1)]
+# Weight-streaming schedule: (1, 4, 1), (16, 32, 4), (100, 40, 4); tiled:
+# (128, 8, 8), (130, 2, 2), (256, 8, 4), (300, 4, 1).
+BLOCK_CASES = [(1, 4, 1), (16, 32, 4), (100, 40, 4), (128, 8, 8), (130, 2, 2), (256, 8, 4),
+               (300, 4, 1)]
 
 
 @pytest.mark.parametrize("T,E,k", BLOCK_CASES)
