@@ -88,8 +88,10 @@ typedef enum moe_status {
   MOE_ERROR_WORKSPACE = 3,     /* ws is NULL or smaller than required         */
   MOE_ERROR_UNSUPPORTED = 4,   /* current device is not gfx950                */
   MOE_ERROR_HIP = 5,           /* a HIP runtime call or launch failed         */
-  MOE_ERROR_LAYOUT = 6         /* a weight descriptor not filled by           */
+  MOE_ERROR_LAYOUT = 6,        /* a weight descriptor not filled by           */
                                /* moe_pack_weights, or of other E / N         */
+  MOE_ERROR_RANGE = 7          /* weights whose scale spread exceeds what the */
+                               /* FP6-piece path is accurate for              */
 } moe_status_t;
 
 /* One packed MXFP4 weight tensor [E, N, K = 2880] (E experts of N rows).
@@ -103,8 +105,13 @@ typedef struct moe_packed_weight {
   int32_t E;              /* experts                                           */
   int32_t N;              /* rows per expert: 5760 (gate/up) or 2880 (down)    */
   uint32_t tag;           /* MOE_PACKED_TAG once packed                        */
-  uint32_t reserved;      /* 0                                                 */
+  uint32_t scale_spread;  /* largest (max - min) of the E8M0 scale exponents   */
+                          /* within one expert (NaN bytes excluded), in binades */
 } moe_packed_weight_t;
+
+/* Largest scale_spread for which the FP6-piece path (moe_forward_mx6 on its
+ * tiled schedule, moe_gate_up_mx6) meets the accuracy bar of moe_forward. */
+#define MOE_MX6_MAX_SCALE_SPREAD 16u
 
 /* The entry points that take a workspace, for moe_workspace_size_op. */
 typedef enum moe_op {
@@ -131,8 +138,10 @@ size_t moe_workspace_size(int T, int E, int k);
 
 /* Packs one MXFP4 weight tensor from the canonical layout into the order the
  * expert GEMMs read (see the conventions above) and fills `desc` (host
- * memory) with the packed arrays, E, N and MOE_PACKED_TAG. N % 64 == 0,
- * 64 <= N <= 65536, 1 <= E <= 256; K = 2880.
+ * memory) with the packed arrays, E, N, MOE_PACKED_TAG and the tensor's
+ * scale_spread. N % 64 == 0, 64 <= N <= 65536, 1 <= E <= 256; K = 2880.
+ * A one-time setup call: it allocates a small device buffer for the scale
+ * ranges and synchronises `stream` before returning.
  *   codes [E, N, 1440] u8, scales [E, N, 90] u8 (canonical, in)
  *   packed_codes, packed_scales: same sizes (out; must not overlap the input)
  *   desc: written only when the call succeeds
@@ -246,9 +255,11 @@ moe_status_t moe_forward(const uint16_t* x, const float* Wr, const float* br,
  * h the same way (rounded to bf16, then encoded by the gate/up kernel as it
  * writes h). The pieces stand for a row to within max|block| / 256 per
  * 32-value block; the layer output stays within the accuracy bar of
- * moe_forward while the weight scales of an expert span up to about 16
- * binades (checkpoint-like weights span a few); past that, use moe_forward.
- * The few-rows-per-expert (decode) schedule is that of moe_forward.
+ * moe_forward while the weight scales of an expert span up to 16 binades
+ * (checkpoint-like weights span a few): where the tiled schedule runs and
+ * w13 or w2 has a scale_spread above MOE_MX6_MAX_SCALE_SPREAD the call is
+ * refused with MOE_ERROR_RANGE (use moe_forward). The few-rows-per-expert
+ * (decode) schedule is that of moe_forward and has no such limit.
  * Arguments and errors as moe_forward; the workspace (moe_workspace_size)
  * also holds the records of x and h. Source: the pages fix MXFP4 weights
  * and their packing for inference (techniques map, "inference & serving");
@@ -284,7 +295,9 @@ moe_status_t moe_encode_mx6(const uint16_t* x, int rows, uint8_t* records, void*
 /* moe_gate_up with the activations given as moe_encode_mx6 records
  * x_records [T, 23, 256] u8 (16-byte aligned) instead of bf16 rows: the
  * block-scaled FP4 x FP6 gate/up GEMM of moe_forward_mx6, always in its tiled
- * schedule. Other arguments, output and errors as moe_gate_up. */
+ * schedule: refused with MOE_ERROR_RANGE when w13's scale_spread exceeds
+ * MOE_MX6_MAX_SCALE_SPREAD. Other arguments, output and errors as
+ * moe_gate_up. */
 moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
                              const int32_t* sorted_rows,
                              const moe_packed_weight_t* w13, const uint16_t* b13,

@@ -102,6 +102,13 @@ class PackedWeight:
             raise ValueError("packed weight descriptor no longer matches its tensors")
         return ctypes.byref(d)
 
+    @property
+    def scale_spread(self) -> int:
+        """Largest spread (max - min, in binades) of the E8M0 scale exponents
+        within one expert; the FP6-piece path refuses more than
+        MOE_MX6_MAX_SCALE_SPREAD."""
+        return int(self._desc.scale_spread)
+
 
 @dataclass(eq=False)
 class PackedExperts:

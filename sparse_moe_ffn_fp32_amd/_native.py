@@ -26,10 +26,12 @@ STATUS_NAMES = {
     4: "MOE_ERROR_UNSUPPORTED",
     5: "MOE_ERROR_HIP",
     6: "MOE_ERROR_LAYOUT",
+    7: "MOE_ERROR_RANGE",
 }
 
 MOE_PACKED_TAG = 0x3450584D
 MOE_NOALLOC_SCRATCH_BYTES = 56 << 20
+MOE_MX6_MAX_SCALE_SPREAD = 16
 
 # moe_op_t: the entry points that take a workspace
 OPS = {"route": 0, "permute": 1, "expert_ffn": 2, "forward": 3, "forward_mx6": 4,
@@ -39,7 +41,7 @@ OPS = {"route": 0, "permute": 1, "expert_ffn": 2, "forward": 3, "forward_mx6": 4
 class PackedWeightDesc(ctypes.Structure):
     """moe_packed_weight_t of include/moe.h."""
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("E", ctypes.c_int32),
-                ("N", ctypes.c_int32), ("tag", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("N", ctypes.c_int32), ("tag", ctypes.c_uint32), ("scale_spread", ctypes.c_uint32)]
 
 _lib = None
 

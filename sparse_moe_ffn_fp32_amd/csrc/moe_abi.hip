@@ -8,6 +8,8 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
+#include <algorithm>
 
 #include "moe.h"
 #include "moe_device.h"
@@ -185,6 +187,8 @@ const char* moe_status_string(moe_status_t status) {
     case MOE_ERROR_HIP: return "MOE_ERROR_HIP: a HIP runtime call or kernel launch failed";
     case MOE_ERROR_LAYOUT:
       return "MOE_ERROR_LAYOUT: weight descriptor not filled by moe_pack_weights or of other E / N";
+    case MOE_ERROR_RANGE:
+      return "MOE_ERROR_RANGE: weight scale spread beyond what the FP6-piece path is accurate for; use moe_forward";
   }
   return "unknown moe_status_t";
 }
@@ -218,12 +222,25 @@ moe_status_t moe_pack_weights(const uint8_t* codes, const uint8_t* scales, int E
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   MOE_TRY(after_launch(moe::launch_pack(codes, scales, E, N, packed_codes, packed_scales, s), s));
+  // the tensor's scale spread, for the FP6-piece path's accuracy limit
+  int32_t* lohi_dev = nullptr;
+  if (hipMalloc(&lohi_dev, sizeof(int32_t) * 2 * E) != hipSuccess) return MOE_ERROR_HIP;
+  std::vector<int32_t> lohi(2 * (size_t)E);
+  hipError_t err = moe::launch_scale_range(scales, E, N, lohi_dev, s);
+  if (err == hipSuccess)
+    err = hipMemcpyAsync(lohi.data(), lohi_dev, sizeof(int32_t) * 2 * E, hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  hipFree(lohi_dev);
+  if (err != hipSuccess) return MOE_ERROR_HIP;
+  uint32_t spread = 0;
+  for (int e = 0; e < E; ++e)
+    if (lohi[2 * e + 1] >= lohi[2 * e]) spread = std::max(spread, (uint32_t)(lohi[2 * e + 1] - lohi[2 * e]));
   desc->codes = packed_codes;
   desc->scales = packed_scales;
   desc->E = E;
   desc->N = N;
   desc->tag = MOE_PACKED_TAG;
-  desc->reserved = 0;
+  desc->scale_spread = spread;
   return MOE_SUCCESS;
 }
 
@@ -292,6 +309,7 @@ moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
   if (T == 0) return MOE_SUCCESS;
   if (!x_records || !offsets || !sorted_rows || !b13 || !h) return MOE_ERROR_INVALID_VALUE;
   MOE_TRY(check_packed(w13, E, moe::kN13));
+  if (w13->scale_spread > MOE_MX6_MAX_SCALE_SPREAD) return MOE_ERROR_RANGE;
   if (!aligned(x_records, 16) || !aligned(h, 16) || !aligned(b13, 8) || !aligned(offsets, 4) ||
       !aligned(sorted_rows, 4))
     return MOE_ERROR_MISALIGNED;
@@ -404,6 +422,11 @@ moe_status_t forward_impl(const uint16_t* x, const float* Wr, const float* br,
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(out, 16) || !aligned(br, 4))
     return MOE_ERROR_MISALIGNED;
   const moe_op_t op = mx6 ? MOE_OP_FORWARD_MX6 : MOE_OP_FORWARD;
+  // the FP6-piece path (tiled schedule only) holds the bar up to a bounded
+  // scale spread
+  if (mx6 && moe::ffn_uses_tiles(T * k, E) &&
+      (lw.w13->scale_spread > MOE_MX6_MAX_SCALE_SPREAD || lw.w2->scale_spread > MOE_MX6_MAX_SCALE_SPREAD))
+    return MOE_ERROR_RANGE;
   MOE_TRY(check_ws(ws, ws_bytes, op, T, E, k));
   MOE_TRY(check_device());
   return forward_launch(x, Wr, br, lw, T, E, k, out, static_cast<char*>(ws), layout(op, T, E, k),

@@ -52,6 +52,8 @@ size_t route_scratch_bytes(int T, int E);
 // canonical MXFP4 codes/scales [E, N, ...] -> the packed order of the GEMMs
 hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, int E, int N, uint8_t* pcodes,
                        uint8_t* pscales, hipStream_t s);
+// smallest and largest E8M0 scale byte (255 excluded) of each expert: lohi [2E]
+hipError_t launch_scale_range(const uint8_t* scales, int E, int N, int32_t* lohi, hipStream_t s);
 
 // Stable permutation of n = T*k slots. Up to 1024 slots (or without hist):
 // one workgroup; above: a histogram pass into hist (ceil(T/32)*E ints), a

@@ -158,6 +158,36 @@ def test_forward_mx6_edge_inputs():
     assert_out_close(np_(out), want, "E=256 k=8")
 
 
+def test_forward_mx6_refuses_wide_scale_spread():
+    """Packing records each tensor's scale spread (the configurations' [-8, -5]
+    gives 3, [-16, 0] 16); past 16 binades (here [-20, 4], 24) the FP6-piece
+    path would miss the bar, so moe_forward_mx6 on its tiled schedule and
+    moe_gate_up_mx6 refuse with MOE_ERROR_RANGE, while the decode schedule
+    (bf16, exact) still runs and meets the oracle."""
+    for rng, want in (((-8, -5), 3), ((-16, 0), 16)):
+        inp = make_layer_inputs(1, 4, 1, seed=77, scale_exp_range=rng)
+        ex = to_device(inp)["experts"]
+        assert ex.w13.scale_spread == want and ex.w2.scale_spread == want, (rng, ex.w13.scale_spread)
+    E, k = 8, 4
+    inp = make_layer_inputs(640, E, k, seed=78, scale_exp_range=(-20, 4))
+    d = to_device(inp)
+    assert d["experts"].w13.scale_spread == 24
+    with pytest.raises(moe.MoeError, match="RANGE"):
+        moe.forward_mx6(d["x"], d["Wr"], d["br"], *weights_args(d), k=k)   # 2560 slots: tiled
+    ids, w = moe.route(d["x"], d["Wr"], d["br"], k=k)
+    counts, offsets, rows = moe.permute(ids, E)
+    with pytest.raises(moe.MoeError, match="RANGE"):
+        moe.gate_up_mx6(moe.encode_mx6(d["x"]), offsets, rows, *weights_args(d), k=k)
+    # 16 tokens: the weight-streaming schedule, the same kernels as moe_forward
+    T = 16
+    dd = {key: (v[:T] if key == "x" else v) for key, v in d.items()}
+    out = moe.forward_mx6(dd["x"], dd["Wr"], dd["br"], *weights_args(dd), k=k)
+    ids, w = moe.route(dd["x"], dd["Wr"], dd["br"], k=k)
+    torch.cuda.synchronize()
+    ref = oracle.forward(dict(inp, x=inp["x"][:T]), k, ids_override=np_(ids))
+    assert_out_close(np_(out), ref["out"], "forward_mx6 decode, wide scale spread")
+
+
 @pytest.mark.parametrize("idx", [2, 3, 4])
 def test_forward_mx6_config_sampled(idx):
     c = LAYER_CONFIGS[idx]
