@@ -56,4 +56,46 @@ hipError_t launch_mx6_encode(const uint16_t* x, int rows, uint8_t* rec, hipStrea
   return hipGetLastError();
 }
 
+// Range of each expert's E8M0 scale bytes (the NaN byte 255 excluded), for
+// the accuracy limit of the FP6-piece path: lohi[2e] = smallest byte,
+// lohi[2e + 1] = largest (255 and 0 when the expert has none).
+__global__ __launch_bounds__(256) void scale_range_init_kernel(int E, int32_t* __restrict__ lohi) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < E) {
+    lohi[2 * e] = 255;
+    lohi[2 * e + 1] = 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void scale_range_kernel(const uint8_t* __restrict__ scales,
+                                                          long long per_expert,
+                                                          int32_t* __restrict__ lohi) {
+  const int e = blockIdx.y;
+  const uint8_t* p = scales + (size_t)e * per_expert;
+  int lo = 255, hi = 0;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < per_expert;
+       i += (long long)gridDim.x * 256) {
+    const int b = p[i];
+    if (b != 255) {
+      lo = min(lo, b);
+      hi = max(hi, b);
+    }
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    lo = min(lo, __shfl_xor(lo, d, 64));
+    hi = max(hi, __shfl_xor(hi, d, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicMin(&lohi[2 * e], lo);
+    atomicMax(&lohi[2 * e + 1], hi);
+  }
+}
+
+hipError_t launch_scale_range(const uint8_t* scales, int E, int N, int32_t* lohi, hipStream_t s) {
+  hipLaunchKernelGGL(scale_range_init_kernel, dim3((E + 255) / 256), dim3(256), 0, s, E, lohi);
+  hipLaunchKernelGGL(scale_range_kernel, dim3(16, E), dim3(256), 0, s, scales, (long long)N * kKB, lohi);
+  return hipGetLastError();
+}
+
 }  // namespace moe
