@@ -28,6 +28,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
 // within an expert, as in the single-workgroup version.
 constexpr int kScanThreads = 1024;
 constexpr int kScatterThreads = 256;
+constexpr int kScanChunk = 32;   // histogram entries a scan thread loads at once
 
 __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int E, int32_t* __restrict__ hist,
                                                                     int nb,
@@ -42,10 +43,17 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int E, int32
   const bool act = sgm < nseg;
   const int per = (nb + nseg - 1) / nseg;
   const int b0 = min(nb, sgm * per), b1 = min(nb, b0 + per);
+  // the segment's counts in chunks of kScanChunk, each chunk's loads all in
+  // flight at once (one memory round trip per chunk)
   int sum = 0;
   if (act) {
-#pragma unroll 16
-    for (int b = b0; b < b1; ++b) sum += hist[(size_t)b * E + e];
+    for (int b = b0; b < b1; b += kScanChunk) {
+      int v[kScanChunk];
+#pragma unroll
+      for (int j = 0; j < kScanChunk; ++j) v[j] = b + j < b1 ? hist[(size_t)(b + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanChunk; ++j) sum += v[j];
+    }
   }
   seg_sum[tid] = act ? sum : 0;
   __syncthreads();
@@ -87,10 +95,15 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int E, int32
   if (act) {
     int run = excl_e[e];
     for (int q = 0; q < sgm; ++q) run += seg_sum[q * E + e];
-    for (int b = b0; b < b1; ++b) {
-      const int h = hist[(size_t)b * E + e];
-      hist[(size_t)b * E + e] = run;
-      run += h;
+    for (int b = b0; b < b1; b += kScanChunk) {
+      int v[kScanChunk];
+#pragma unroll
+      for (int j = 0; j < kScanChunk; ++j) v[j] = b + j < b1 ? hist[(size_t)(b + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanChunk; ++j) {
+        if (b + j < b1) hist[(size_t)(b + j) * E + e] = run;
+        run += v[j];
+      }
     }
   }
 }
