@@ -24,7 +24,9 @@ CPU implementation).
 
 Also reported: p10/p50/p90 of single steps (a second pass with one event
 pair per step) and, for the weight-bound shapes, the step time without
-rotating weight copies.
+rotating weight copies and the time per layer step when 24 steps (a decode
+pass through gpt-oss-20b's 24 MoE layers) are captured as one HIP graph and
+replayed (`graph_ms_per_step`).
 """
 from __future__ import annotations
 
@@ -191,8 +193,12 @@ def measure(idx, args, dev, steps, warmup, want_kernel=True):
             return
         fwd(x, w["Wr"], w["br"], w["experts"], k=k, out=out, workspace=ws)
 
-    if args.graph:
-        eager_step = step
+    eager_step = step
+
+    def capture_pass(n_layers):
+        """One HIP graph of n_layers consecutive layer steps (a decode pass
+        through that many MoE layers; the weight copies rotate as the layers'
+        weights would)."""
         for i in range(copies):
             eager_step(i)
         torch.cuda.synchronize()
@@ -203,44 +209,64 @@ def measure(idx, args, dev, steps, warmup, want_kernel=True):
                 eager_step(i)
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        graphs = []
-        for i in range(copies):
-            gph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gph):
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            for i in range(n_layers):
                 eager_step(i)
-            graphs.append(gph)
+        return gph
 
-        def step(i):
-            graphs[i % copies].replay()
+    def graph_ms_per_layer(n_layers, layer_steps):
+        gph = capture_pass(n_layers)
+        reps = max(2, layer_steps // n_layers)
+        for _ in range(2):
+            gph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            gph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        del gph
+        return g0.elapsed_time(g1) / (reps * n_layers)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / steps
-    log(f"bench: {ms_per_step * 1e3:.1f} us per step")
-    assert torch.isfinite(out).all().item(), "non-finite layer output"
+    if args.graph:
+        # whole captured passes replayed: time per layer step = replay time /
+        # layers in the pass (no per-step distribution: a replay is one unit)
+        ms_per_step = graph_ms_per_layer(args.graph_layers, steps)
+        p10 = p50 = p90 = ms_per_step
+        log(f"bench: {ms_per_step * 1e3:.1f} us per layer step ({args.graph_layers}-layer graphs)")
+    else:
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = t0.elapsed_time(t1) / steps
+        log(f"bench: {ms_per_step * 1e3:.1f} us per step")
 
-    # Distribution of single steps (a second pass, one event pair per step),
-    # and for the weight-bound shapes the same layer without rotating the
-    # weight copies (one copy, partly served from the Infinity Cache).
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    evs[0].record(stream)
-    for i in range(steps):
-        step(i)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
-    p10, p50, p90 = (float(v) for v in np.percentile(per_step, [10, 50, 90]))
+        # Distribution of single steps (a second pass, one event pair per
+        # step), and for the weight-bound shapes the same layer without
+        # rotating the weight copies (one copy, partly served from the
+        # Infinity Cache).
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(stream)
+        for i in range(steps):
+            step(i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+        p10, p50, p90 = (float(v) for v in np.percentile(per_step, [10, 50, 90]))
+    assert torch.isfinite(out).all().item(), "non-finite layer output"
     nonrot_ms = None
-    if copies > 1:
+    if copies > 1 and not args.graph:
         n0 = torch.cuda.Event(enable_timing=True)
         n1 = torch.cuda.Event(enable_timing=True)
         n0.record(stream)
@@ -249,6 +275,14 @@ def measure(idx, args, dev, steps, warmup, want_kernel=True):
         n1.record(stream)
         torch.cuda.synchronize()
         nonrot_ms = n0.elapsed_time(n1) / steps
+
+    # Decode shapes: the same layer steps captured as one HIP graph per decode
+    # pass through the model's MoE layers (gpt-oss-20b: 24 layers, its raw
+    # config.json), replayed; time per layer step.
+    graph_ms = None
+    if cfg.regime == "decode" and not args.graph:
+        graph_ms = graph_ms_per_layer(24, 24 * 20)
+        log(f"bench: {graph_ms * 1e3:.1f} us per layer step replaying 24-layer graphs")
 
     # Dominant kernel: the gate/up GEMM, timed by HIP events on its stream
     # around back-to-back launches (the routing is computed once; each launch
@@ -330,6 +364,7 @@ def measure(idx, args, dev, steps, warmup, want_kernel=True):
         "layer_roofline_unit": layer_unit, "experts_touched": touched,
         "p10_p50_p90": [p10, p50, p90], "nonrot_ms": nonrot_ms,
         "kernel_ms": kern_ms, "layer_flop": layer_flop, "layer_alg_bytes": layer_alg_bytes,
+        "graph_ms": graph_ms,
     }
     del sets, x, out, ws
     torch.cuda.empty_cache()
@@ -357,8 +392,11 @@ def main() -> int:
                          "MX FP6 activations with the block-scaled FP4 matrix cores "
                          "(moe_forward_mx6)")
     ap.add_argument("--graph", action="store_true",
-                    help="capture each step (one per weight copy) into a HIP graph once and time "
-                         "the replays")
+                    help="capture --graph-layers consecutive steps (a decode pass through that many "
+                         "MoE layers, weight copies rotating) into one HIP graph and time its "
+                         "replays per layer step")
+    ap.add_argument("--graph-layers", type=int, default=24,
+                    help="layer steps per captured graph (gpt-oss-20b has 24 layers)")
     ap.add_argument("--block", action="store_true",
                     help="time the decoder sublayer x + layer(RMSNorm(x)) (moe_forward_block) "
                          "instead of the layer alone")
@@ -411,6 +449,7 @@ def main() -> int:
         "experts_touched": r["experts_touched"],
         "step_ms_p10_p50_p90": [round(v, 5) for v in r["p10_p50_p90"]],
         "ms_per_step_one_weight_copy": None if r["nonrot_ms"] is None else round(r["nonrot_ms"], 5),
+        "graph_ms_per_step": None if r["graph_ms"] is None else round(r["graph_ms"], 5),
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_per_config:
@@ -430,6 +469,13 @@ def main() -> int:
                 "layer_roofline_unit": ri["layer_roofline_unit"],
                 "weight_copies_rotated": ri["copies"],
             }
+            if ri["graph_ms"] is not None:
+                g = ri["graph_ms"]
+                per[str(idx)].update({
+                    "graph_ms_per_step": round(g, 5),
+                    "graph_tokens_per_s": round(ri["T"] / (g * 1e-3), 1),
+                    "graph_layer_roofline_frac": round(ri["layer_alg_bytes"] / (g * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "graph": "24 layer steps per HIP graph (one decode pass), replayed"})
         res["per_config"] = per
     if not args.no_peak_probe:
         peaks = measured_peaks(dev)
