@@ -84,3 +84,47 @@ def test_forward_graph_replays(T, E, k, path):
         ref = oracle.forward(inp, k, ids_override=ids.cpu().numpy())
         check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["logits"], k)
         assert_out_close(got.cpu().numpy(), ref["out"], f"graph replay, {path}")
+
+
+def test_forward_graph_pass_of_layers():
+    """Three layer steps with different weights (a decode pass through three
+    MoE layers, T=64, E=32) captured in one graph, one workspace shared: every
+    replay reproduces each layer's eager output bit for bit, and the first
+    layer's output meets the bar against the oracle."""
+    T, E, k = 64, 32, 4
+    print(f"graph pass: 3 layers T={T} E={E} k={k}", flush=True)
+    inps = [make_layer_inputs(T, E, k, seed=9100 + j) for j in range(3)]
+    ds = [to_device(inp) for inp in inps]
+    x = ds[0]["x"]
+    ws = torch.empty(moe.workspace_size(T, E, k), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((T, 2880), dtype=torch.float32, device="cuda") for _ in range(3)]
+
+    def layers():
+        for d, out in zip(ds, outs):
+            moe.forward(x, d["Wr"], d["br"], *weights_args(d), k=k, out=out, workspace=ws)
+
+    layers()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layers()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layers()
+    for r in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        ws.fill_(0xCD)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), f"replay {r}, layer {j} differs"
+    ids, w = moe.route(x, ds[0]["Wr"], ds[0]["br"], k=k)
+    ref = oracle.forward(dict(inps[0], x=inps[0]["x"]), k, ids_override=ids.cpu().numpy())
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref["logits"], k)
+    assert_out_close(outs[0].cpu().numpy(), ref["out"], "graph pass, layer 0")
