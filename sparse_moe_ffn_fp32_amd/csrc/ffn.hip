@@ -365,9 +365,8 @@ __global__ __launch_bounds__(kSkThreads) void ffn_skinny_kernel(FfnArgs a) {
         const float v2 = acc[mt][nt][2] + bf16_bits_to_f32(braw[mt].y & 0xFFFFu);
         const float v3 = acc[mt][nt][3] + bf16_bits_to_f32(braw[mt].y >> 16);
         if constexpr (EPI == EPI_SWIGLU) {
-          const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(v0, v1));
-          const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(v2, v3));
-          *reinterpret_cast<uint32_t*>(a.h_out + (size_t)p * kI + R0 / 2) = h0 | (h1 << 16);
+          *reinterpret_cast<uint32_t*>(a.h_out + (size_t)p * kI + R0 / 2) =
+              f32x2_to_bf16x2_bits(swiglu_pair(v0, v1), swiglu_pair(v2, v3));
         } else if constexpr (EPI == EPI_COMBINE) {
           float* o = a.out + (size_t)(slot[nt] / a.k) * kH + R0;
           unsafeAtomicAdd(o + 0, wt[nt] * v0);
@@ -625,9 +624,8 @@ __device__ __forceinline__ void wide6_body(const FfnArgs& a) {
 #pragma unroll
           for (int nt = 0; nt < kWdNT; ++nt) {
             const f32x4& c = acc[mt][nt];
-            const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(c[0] + b[0], c[1] + b[1]));
-            const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(c[2] + b[2], c[3] + b[3]));
-            *reinterpret_cast<uint32_t*>(hs + (16 * nt + r) * 64 + (8 * mt + 2 * g) * 2) = h0 | (h1 << 16);
+            *reinterpret_cast<uint32_t*>(hs + (16 * nt + r) * 64 + (8 * mt + 2 * g) * 2) =
+                f32x2_to_bf16x2_bits(swiglu_pair(c[0] + b[0], c[1] + b[1]), swiglu_pair(c[2] + b[2], c[3] + b[3]));
           }
         }
         float v[32];
@@ -668,9 +666,8 @@ __device__ __forceinline__ void wide6_body(const FfnArgs& a) {
         const int p = rb + 16 * nt + r;
         if (p >= re) continue;
         const f32x4& c = acc[mt][nt];
-        const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(c[0] + b[0], c[1] + b[1]));
-        const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(c[2] + b[2], c[3] + b[3]));
-        *reinterpret_cast<uint32_t*>(a.h_out + (size_t)p * kI + R0 / 2) = h0 | (h1 << 16);
+        *reinterpret_cast<uint32_t*>(a.h_out + (size_t)p * kI + R0 / 2) =
+            f32x2_to_bf16x2_bits(swiglu_pair(c[0] + b[0], c[1] + b[1]), swiglu_pair(c[2] + b[2], c[3] + b[3]));
       }
     }
   } else {
@@ -726,6 +723,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
 // hit 64 distinct banks in every LDS cycle (measured conflict-free).
 // A tile with at most 64 tokens (an expert's last) runs only its first two
 // token tiles.
+// The last column block of a projection holds fewer than 8 groups (N = 5,760:
+// 2 of 8; N = 2,880: 5 of 8). With one group per wave its busiest SIMD
+// would carry a full block's work, so there the token tiles are split across
+// waves (tl_wave_role): each wave then takes one group and one or more
+// consecutive 32-token tiles, which evens out the SIMDs (waves w and w + 4
+// share one).
 constexpr int kTlBT = 128;                       // tokens per tile
 constexpr int kTlWaves = 8;                      // waves per block, one 64-row group each
 constexpr int kTlThreads = 64 * kTlWaves;
@@ -841,10 +844,13 @@ __host__ __device__ constexpr int tl_wait_mid(int s) {
        : tl_issued_after_barrier(s - 1);
 }
 
-template <int EPI, int NTA, bool W_OK>
+// tile_run: NTL = 32-token tiles of the block's tile that are loaded (4, or
+// 2 for a tile of at most 64 tokens); this wave computes NTA of them from
+// tile nt0 on, for weight group G (local group gloc of the column block).
+template <int EPI, int NTL, int NTA, bool W_OK>
 __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const int* slot_of,
                                          int* xrow_of, const uint16_t* bias_s, int e, int G,
-                                         int rb, int re) {
+                                         int gloc, int nt0, int rb, int re) {
   constexpr bool w_ok = W_OK;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -859,7 +865,7 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
   // last piece. The instructions whose rows lie in token tiles a half tile
   // skips are not issued.
   const int q_lds = lane & 15;
-  constexpr int kLoadRows = NTA * 32;
+  constexpr int kLoadRows = NTL * 32;
   const uint16_t* xsrc[kTlXLoads];   // this lane's row (and K piece) per instruction
 #pragma unroll
   for (int j = 0; j < kTlXLoads; ++j) {
@@ -899,11 +905,13 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
   // slot, half by half once each half has been consumed) are spread over the
   // substeps, so the wave keeps the matrix cores fed while its memory
   // instructions wait to issue.
+  // this wave's activation rows: token tiles nt0 .. nt0 + NTA - 1
+  const int xrow0 = (32 * nt0 + c) * kXRow;
   auto read_x = [&](const uint8_t* xsb, int q, bf16x8 (&xf)[NTA]) __attribute__((always_inline)) {
     const int jb = q >> 2, i = q & 3;
 #pragma unroll
     for (int nt = 0; nt < NTA; ++nt)
-      xf[nt] = *reinterpret_cast<const bf16x8*>(xsb + (32 * nt + c) * kXRow +
+      xf[nt] = *reinterpret_cast<const bf16x8*>(xsb + xrow0 + 32 * nt * kXRow +
                                                 (((8 * jb + 4 * h + i) ^ rr) * 16));
   };
   auto wait_for = [&](int n) __attribute__((always_inline)) {
@@ -954,7 +962,7 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
         if (next_here || next_step) {
           const uint8_t* src = next_here ? xsb : stage(s + 1);
           const int qn = next_here ? q + 1 : 0;
-          xf[nt] = *reinterpret_cast<const bf16x8*>(src + (32 * nt + c) * kXRow +
+          xf[nt] = *reinterpret_cast<const bf16x8*>(src + xrow0 + 32 * nt * kXRow +
                                                     (((8 * (qn >> 2) + 4 * h + (qn & 3)) ^ rr) * 16));
         }
       }
@@ -993,13 +1001,14 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
   });
   static_assert(tl_wait_mid(0) == 4 && tl_wait_mid(1) == 10 && tl_wait_mid(10) == 10 &&
                 tl_wait_mid(20) == 10 && tl_wait_mid(21) == 3, "load accounting");
+
   if (!w_ok) return;
 
   // D[weight row][token]: lane holds token column c of tile nt and weight
   // rows 32mt + 8q + 4h + j (j = 0..3) of the wave's group
 #pragma unroll
   for (int nt = 0; nt < NTA; ++nt) {
-    const int t = 32 * nt + c;
+    const int t = 32 * (nt0 + nt) + c;
     if (rb + t >= re) continue;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -1007,15 +1016,14 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
       for (int q = 0; q < 4; ++q) {
         const int lr = 32 * mt + 8 * q + 4 * h;   // row within the group
         const f32x16& A = acc[mt][nt];
-        const float v0 = A[4 * q + 0] + bf16_bits_to_f32(bias_s[wave * 64 + lr + 0]);
-        const float v1 = A[4 * q + 1] + bf16_bits_to_f32(bias_s[wave * 64 + lr + 1]);
-        const float v2 = A[4 * q + 2] + bf16_bits_to_f32(bias_s[wave * 64 + lr + 2]);
-        const float v3 = A[4 * q + 3] + bf16_bits_to_f32(bias_s[wave * 64 + lr + 3]);
+        const float v0 = A[4 * q + 0] + bf16_bits_to_f32(bias_s[gloc * 64 + lr + 0]);
+        const float v1 = A[4 * q + 1] + bf16_bits_to_f32(bias_s[gloc * 64 + lr + 1]);
+        const float v2 = A[4 * q + 2] + bf16_bits_to_f32(bias_s[gloc * 64 + lr + 2]);
+        const float v3 = A[4 * q + 3] + bf16_bits_to_f32(bias_s[gloc * 64 + lr + 3]);
         const int R0 = G * 64 + lr;
         if constexpr (EPI == EPI_SWIGLU) {
-          const uint32_t h0 = f32_to_bf16_bits(swiglu_pair(v0, v1));
-          const uint32_t h1 = f32_to_bf16_bits(swiglu_pair(v2, v3));
-          *reinterpret_cast<uint32_t*>(a.h_out + (size_t)(rb + t) * kI + R0 / 2) = h0 | (h1 << 16);
+          *reinterpret_cast<uint32_t*>(a.h_out + (size_t)(rb + t) * kI + R0 / 2) =
+              f32x2_to_bf16x2_bits(swiglu_pair(v0, v1), swiglu_pair(v2, v3));
         } else if constexpr (EPI == EPI_COMBINE) {
           const int slot = slot_of[t];
           const float wt = a.topk_w[slot];
@@ -1030,6 +1038,35 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
       }
     }
   }
+}
+
+// What wave `wave` computes in a column block of gl valid 64-row groups
+// (1 .. 8) over a tile of ntl loaded 32-token tiles: 0 = group gloc, all ntl
+// token tiles; 1 = group gloc, token tile nt0 only; 2 = nothing (the wave
+// still loads its share of the activation tile). Waves w and w + 4 share a
+// SIMD.
+__device__ __forceinline__ int tl_wave_role(int gl, int ntl, int wave, int& gloc, int& nt0) {
+  gloc = wave;
+  nt0 = 0;
+  if (gl >= kTlWaves) return 0;
+  if (gl <= 2) {
+    // each group's token tiles on waves of their own: at most one token
+    // tile per wave
+    if (wave >= gl * ntl) return 2;
+    gloc = wave % gl;
+    nt0 = wave / gl;
+    return 1;
+  }
+  if (gl == 5) {
+    // four whole groups on waves 0..3, one per SIMD; the fifth group's
+    // token tiles on waves 4.., one each
+    if (wave < 4) return 0;
+    if (wave - 4 >= ntl) return 2;
+    gloc = 4;
+    nt0 = wave - 4;
+    return 1;
+  }
+  return wave < gl ? 0 : 2;
 }
 
 template <int EPI>
@@ -1049,9 +1086,14 @@ __global__ __launch_bounds__(kTlThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int total = count_tiles(a.offsets, a.E, kTlBT);
   if (!tile_work_item<kTlChunk>(gx, total, wx, ty)) return;
   find_tile(a.offsets, a.E, kTlBT, ty, e, rb, re);
-  const int G = wx * kTlWaves + wave;
-  const bool w_ok = G < (a.N >> 6);
   const int nvalid = re - rb;
+  const int ntl = nvalid > 64 ? 4 : 2;
+  const int gl = min(kTlWaves, (a.N >> 6) - wx * kTlWaves);
+  int gloc, nt0;
+  const int role = __builtin_amdgcn_readfirstlane(tl_wave_role(gl, ntl, wave, gloc, nt0));
+  gloc = __builtin_amdgcn_readfirstlane(gloc);
+  nt0 = __builtin_amdgcn_readfirstlane(nt0);
+  const int G = wx * kTlWaves + gloc;
   if (tid < kTlBT) slot_of[tid] = tid < nvalid ? a.sorted_rows[rb + tid] : -1;
   {
     const int row = wx * kTlRows + tid;
@@ -1064,12 +1106,14 @@ __global__ __launch_bounds__(kTlThreads) __attribute__((amdgpu_waves_per_eu(2)))
     xrow_of[tid] = a.gather ? slot_of[tv] / a.k : rb + tv;
   }
   __syncthreads();
-  if (__builtin_amdgcn_readfirstlane(w_ok ? 1 : 0)) {
-    if (nvalid > 64) tile_run<EPI, 4, true>(a, xs, slot_of, xrow_of, bias_s, e, G, rb, re);
-    else tile_run<EPI, 2, true>(a, xs, slot_of, xrow_of, bias_s, e, G, rb, re);
+  if (ntl == 4) {
+    if (role == 0) tile_run<EPI, 4, 4, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, 0, rb, re);
+    else if (role == 1) tile_run<EPI, 4, 1, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re);
+    else tile_run<EPI, 4, 1, false>(a, xs, slot_of, xrow_of, bias_s, e, 0, 0, 0, rb, re);
   } else {
-    if (nvalid > 64) tile_run<EPI, 4, false>(a, xs, slot_of, xrow_of, bias_s, e, G, rb, re);
-    else tile_run<EPI, 2, false>(a, xs, slot_of, xrow_of, bias_s, e, G, rb, re);
+    if (role == 0) tile_run<EPI, 2, 2, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, 0, rb, re);
+    else if (role == 1) tile_run<EPI, 2, 1, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re);
+    else tile_run<EPI, 2, 1, false>(a, xs, slot_of, xrow_of, bias_s, e, 0, 0, 0, rb, re);
   }
 }
 

@@ -63,8 +63,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
 
 // Round-to-nearest-even float -> bf16 bits (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two floats -> packed bf16 bits, lo in the low half (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2));
 }
 
 // E8M0 byte -> the fp32 scale 2^(s-127) (s in [1, 254]).
@@ -92,10 +97,13 @@ __device__ __forceinline__ bf16x8 u4_as_bf16x8(uint4 v) {
 
 // gpt-oss gated unit for one (gate, up) pair, after the bias.
 __device__ __forceinline__ float swiglu_pair(float gate, float up) {
+  constexpr float kNegAlphaLog2e = -kSwigluAlpha * 1.44269504088896341f;
   gate = fminf(gate, kSwigluLimit);
   up = fminf(fmaxf(up, -kSwigluLimit), kSwigluLimit);
-  float glu = gate / (1.0f + __expf(-kSwigluAlpha * gate));
-  return (up + 1.0f) * glu;
+  // sigma(alpha * gate) = 1 / (1 + 2^(-alpha * log2(e) * gate)) on v_exp_f32
+  // and v_rcp_f32 (about 1 ulp each; the result is rounded to bf16)
+  const float glu = gate * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gate * kNegAlphaLog2e));
+  return fmaf(up, glu, glu);   // (up + 1) * glu
 }
 
 // Locate token tile `tile` of a grouped GEMM whose experts own the row ranges

@@ -56,8 +56,8 @@ __device__ __forceinline__ uint4 norm_apply8(const uint4 d, float inv, const flo
   uint32_t o[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    o[q] = f32_to_bf16_bits(bf16_bits_to_f32(dw[q] & 0xFFFFu) * inv * s[2 * q]) |
-           (f32_to_bf16_bits(bf16_bits_to_f32(dw[q] >> 16) * inv * s[2 * q + 1]) << 16);
+    o[q] = f32x2_to_bf16x2_bits(bf16_bits_to_f32(dw[q] & 0xFFFFu) * inv * s[2 * q],
+                                bf16_bits_to_f32(dw[q] >> 16) * inv * s[2 * q + 1]);
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
