@@ -894,11 +894,7 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
   TlWeights wsrc;
   wsrc.init(a, e, w_ok ? G : 0, lane);
   TlStep wq[2];
-  f32x16 acc[2][NTA];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NTA; ++nt) acc[mt][nt] = f32x16{};
+  f32x16 acc[2][NTA];   // set from the biases once the first loads are issued
 
   // One K step: 8 substeps (jb, i) of 2 x NTA MFMAs each. The activation DMA
   // of step s + 3 and the weights of step s + 2 (into this step's register
@@ -989,6 +985,20 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
   for (int s = 0; s < kTlStages - 1; ++s)
 #pragma unroll
     for (int j = 0; j < kTlXLoads; ++j) load_x_one(stage(s), s, j);
+  // D[weight row][token]: lane holds token column c of tile nt and weight
+  // rows 32mt + 8q + 4h + j (j = 0..3) of the wave's group. The accumulators
+  // start from the rows' biases (while the first loads are in flight), so the
+  // epilogue has no bias to add.
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float b = w_ok ? bf16_bits_to_f32(bias_s[gloc * 64 + 32 * mt + 8 * q + 4 * h + j]) : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NTA; ++nt) acc[mt][nt][4 * q + j] = b;
+      }
   wait_for(2 * kTlXLoads);   // X(0) and both weight steps
   __builtin_amdgcn_s_barrier();
   read_x(stage(0), 0, xf);
@@ -1024,11 +1034,10 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int lr = 32 * mt + 8 * q + 4 * h;   // row within the group
           const f32x16& A = acc[mt][nt];
           float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = A[4 * q + j] + bf16_bits_to_f32(bias_s[gloc * 64 + lr + j]);
+          for (int j = 0; j < 4; ++j) v[j] = A[4 * q + j];
           const int u = 8 * mt + 2 * q + h;
           *reinterpret_cast<float4*>(own + c * 256 + 16 * (u ^ (c & 15))) = make_float4(v[0], v[1], v[2], v[3]);
         }
@@ -1047,8 +1056,6 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
     return;
   }
 
-  // D[weight row][token]: lane holds token column c of tile nt and weight
-  // rows 32mt + 8q + 4h + j (j = 0..3) of the wave's group
 #pragma unroll
   for (int nt = 0; nt < NTA; ++nt) {
     const int t = 32 * (nt0 + nt) + c;
@@ -1059,10 +1066,7 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
       for (int q = 0; q < 4; ++q) {
         const int lr = 32 * mt + 8 * q + 4 * h;   // row within the group
         const f32x16& A = acc[mt][nt];
-        const float v0 = A[4 * q + 0] + bf16_bits_to_f32(bias_s[gloc * 64 + lr + 0]);
-        const float v1 = A[4 * q + 1] + bf16_bits_to_f32(bias_s[gloc * 64 + lr + 1]);
-        const float v2 = A[4 * q + 2] + bf16_bits_to_f32(bias_s[gloc * 64 + lr + 2]);
-        const float v3 = A[4 * q + 3] + bf16_bits_to_f32(bias_s[gloc * 64 + lr + 3]);
+        const float v0 = A[4 * q + 0], v1 = A[4 * q + 1], v2 = A[4 * q + 2], v3 = A[4 * q + 3];
         const int R0 = G * 64 + lr;
         if constexpr (EPI == EPI_SWIGLU) {
           *reinterpret_cast<uint32_t*>(a.h_out + (size_t)(rb + t) * kI + R0 / 2) =
@@ -1112,6 +1116,21 @@ __device__ __forceinline__ int tl_wave_role(int gl, int ntl, int wave, int& gloc
   return wave < gl ? 0 : 2;
 }
 
+// The instance of tile_run for a wave's role (tl_wave_role) in a tile of NTL
+// loaded 32-token tiles; with one token tile roles 0 and 1 coincide.
+template <int EPI, int NTL>
+__device__ __forceinline__ void tile_roles(int role, const FfnArgs& a, uint8_t* xs, const int* slot_of,
+                                           int* xrow_of, const uint16_t* bias_s, int e, int G,
+                                           int gloc, int nt0, int rb, int re) {
+  if (role == 2) {
+    tile_run<EPI, NTL, 1, false>(a, xs, slot_of, xrow_of, bias_s, e, 0, 0, 0, rb, re);
+  } else if (NTL == 1 || role == 1) {
+    tile_run<EPI, NTL, 1, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re);
+  } else {
+    tile_run<EPI, NTL, NTL, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, 0, rb, re);
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(kTlThreads) __attribute__((amdgpu_waves_per_eu(2))) void ffn_tile_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t xs[kTlStages * kTlStage];
@@ -1130,7 +1149,7 @@ __global__ __launch_bounds__(kTlThreads) __attribute__((amdgpu_waves_per_eu(2)))
   if (!tile_work_item<kTlChunk>(gx, total, wx, ty)) return;
   find_tile(a.offsets, a.E, kTlBT, ty, e, rb, re);
   const int nvalid = re - rb;
-  const int ntl = nvalid > 64 ? 4 : 2;
+  const int ntl = (nvalid + 31) >> 5;   // 32-token tiles that hold rows (1..4)
   const int gl = min(kTlWaves, (a.N >> 6) - wx * kTlWaves);
   int gloc, nt0;
   const int role = __builtin_amdgcn_readfirstlane(tl_wave_role(gl, ntl, wave, gloc, nt0));
@@ -1149,14 +1168,11 @@ __global__ __launch_bounds__(kTlThreads) __attribute__((amdgpu_waves_per_eu(2)))
     xrow_of[tid] = a.gather ? slot_of[tv] / a.k : rb + tv;
   }
   __syncthreads();
-  if (ntl == 4) {
-    if (role == 0) tile_run<EPI, 4, 4, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, 0, rb, re);
-    else if (role == 1) tile_run<EPI, 4, 1, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re);
-    else tile_run<EPI, 4, 1, false>(a, xs, slot_of, xrow_of, bias_s, e, 0, 0, 0, rb, re);
-  } else {
-    if (role == 0) tile_run<EPI, 2, 2, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, 0, rb, re);
-    else if (role == 1) tile_run<EPI, 2, 1, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re);
-    else tile_run<EPI, 2, 1, false>(a, xs, slot_of, xrow_of, bias_s, e, 0, 0, 0, rb, re);
+  switch (ntl) {
+    case 4: tile_roles<EPI, 4>(role, a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re); break;
+    case 3: tile_roles<EPI, 3>(role, a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re); break;
+    case 2: tile_roles<EPI, 2>(role, a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re); break;
+    default: tile_roles<EPI, 1>(role, a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re); break;
   }
 }
 
