@@ -17,6 +17,7 @@ from .moe_oracle import (  # noqa: F401
     forward,
     route,
     router_logits,
+    router_logits_f64,
     router_parameter_shapes,
     routing_weights,
     select_topk,

@@ -6,7 +6,7 @@ TEST INFRASTRUCTURE, under the same rules as ``oracle.moe_oracle``: only
 leg may import it; the product path never does.
 
   t   = RMSNorm(x) = x / sqrt(mean(x^2) + eps) * scale     (per token, over H)
-  out = x + MoE(bf16(t))
+  out = x + MoE(t), the router on t, the experts on bf16(t)
 
 Sources: the "gpt-oss-20b" page (neurarch.com), "Structure" table: every
 decoder layer runs RMSNorm_i_2 -> MoE_i -> Add_i_ffn, i.e. the MoE sees the
@@ -15,9 +15,11 @@ normed hidden state and its output is added to the un-normed one; the
 the GPT-OSS 20B / 120B raw config.json tables (rms_norm_eps = 1e-5).
 Readings where the pages are silent: RMSNorm is the textbook
 x / sqrt(mean(x^2) + eps) * scale with a float32 scale vector of H values;
-the normed activations are rounded to bf16 (the layer's input type, round to
-nearest even) before the router and the experts see them; the residual is
-the bf16 block input x, added in float to the float32 layer output.
+the router, a float32 linear layer with float32 weights, takes the normed
+activations as they are (unrounded; float64 here); the expert GEMMs take them
+rounded once to bf16 (round to nearest even), their matrix-core input type,
+as they take h; the residual is the bf16 block input x, added in float to the
+float32 layer output.
 """
 from __future__ import annotations
 
@@ -58,7 +60,7 @@ def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
 
 def normed_input_bits(x_bits: np.ndarray, scale: np.ndarray,
                       eps: float = RMS_NORM_EPS) -> np.ndarray:
-    """bf16(RMSNorm(x)): the activations the router and the experts see."""
+    """bf16(RMSNorm(x)): the activations the expert GEMMs see."""
     return f64_to_bf16_bits(rmsnorm(x_bits, scale, eps))
 
 
@@ -66,10 +68,13 @@ def block_forward(inputs: Dict[str, np.ndarray], k: int, scale: np.ndarray,
                   eps: float = RMS_NORM_EPS,
                   tokens: Optional[Sequence[int]] = None,
                   ids_override: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """out = x + MoE(bf16(RMSNorm(x))) in float64; also returns the normed
-    bf16 input ("t") and everything ``moe_oracle.forward`` returns for it."""
-    t_bits = normed_input_bits(inputs["x"], scale, eps)
-    res = om.forward(dict(inputs, x=t_bits), k, tokens=tokens, ids_override=ids_override)
+    """out = x + MoE(RMSNorm(x)) in float64, routed on the normed input and
+    with bf16(RMSNorm(x)) into the experts; also returns that bf16 input
+    ("t") and everything ``moe_oracle.forward`` returns for it."""
+    t = rmsnorm(inputs["x"], scale, eps)
+    t_bits = f64_to_bf16_bits(t)
+    res = om.forward(dict(inputs, x=t_bits), k, tokens=tokens, ids_override=ids_override,
+                     router_x=t)
     res["out"] = res["out"] + om.bf16_to_f64(inputs["x"][res["tokens"]])
     res["t"] = t_bits
     return res

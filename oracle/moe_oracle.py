@@ -99,8 +99,13 @@ def router_parameter_shapes(H: int, E: int) -> Dict[str, tuple]:
 
 
 def router_logits(x_bits: np.ndarray, Wr: np.ndarray, br: np.ndarray) -> np.ndarray:
-    x = bf16_to_f64(x_bits)
-    return x @ np.asarray(Wr, dtype=np.float64).T + np.asarray(br, dtype=np.float64)
+    return router_logits_f64(bf16_to_f64(x_bits), Wr, br)
+
+
+def router_logits_f64(x: np.ndarray, Wr: np.ndarray, br: np.ndarray) -> np.ndarray:
+    """The router linear layer on float64 activations."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(Wr, dtype=np.float64).T + \
+        np.asarray(br, dtype=np.float64)
 
 
 def select_topk(logits: np.ndarray, k: int):
@@ -176,8 +181,13 @@ def forward(inputs: Dict[str, np.ndarray], k: int,
             tokens: Optional[Sequence[int]] = None,
             ids_override: Optional[np.ndarray] = None,
             alpha: float = SWIGLU_ALPHA, limit: float = SWIGLU_LIMIT,
-            keep_y: bool = False) -> Dict[str, np.ndarray]:
+            keep_y: bool = False,
+            router_x: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """The whole layer in float64.
+
+    ``router_x`` (float64 [T, H]), when given, is what the router sees in
+    place of the bf16 ``x``; the experts still take ``x`` (the decoder block
+    routes on its unrounded normed input, oracle/block.py).
 
     ``tokens`` restricts the expert computation to those token indices (the
     routing is still computed for every token); ``ids_override`` [T, k]
@@ -185,7 +195,10 @@ def forward(inputs: Dict[str, np.ndarray], k: int,
     of the float64 logits of the given experts). Only experts that some
     computed token selects are dequantised, one at a time.
     """
-    logits = router_logits(inputs["x"], inputs["Wr"], inputs["br"])
+    if router_x is None:
+        logits = router_logits(inputs["x"], inputs["Wr"], inputs["br"])
+    else:
+        logits = router_logits_f64(router_x, inputs["Wr"], inputs["br"])
     T, E = logits.shape
     ids, gap = select_topk(logits, k)
     if ids_override is not None:

@@ -67,8 +67,8 @@ def check_block_residual_and_zero_experts():
     inp["w2_codes"][:] = 0
     g = np.random.default_rng(4).uniform(0.5, 2.0, 2880)
     res = ob.block_forward(inp, k, g)
-    t = ob.normed_input_bits(inp["x"], g)
-    logits = om.bf16_to_f64(t) @ inp["Wr"].astype(np.float64).T + inp["br"].astype(np.float64)
+    t = ob.rmsnorm(inp["x"], g)   # the router sees the unrounded normed input
+    logits = t @ inp["Wr"].astype(np.float64).T + inp["br"].astype(np.float64)
     ids = np.argsort(-logits, axis=1, kind="stable")[:, :k]
     z = np.exp(np.take_along_axis(logits, ids, 1) - np.take_along_axis(logits, ids, 1)[:, :1])
     w = z / z.sum(axis=1, keepdims=True)
@@ -76,6 +76,29 @@ def check_block_residual_and_zero_experts():
     assert np.allclose(res["out"], want, rtol=1e-12, atol=1e-12)
 
 
+def check_block_routes_on_unrounded_norm():
+    """A constant row of ones normalises to 1/sqrt(1 + eps) = 0.999995, which
+    bf16 rounds to 1.0. Expert 0 scores the row's mean, expert 1 a constant
+    0.9999975 between the two: routing on the unrounded value picks expert 1,
+    on the bf16 value expert 0. The expert part is zero (zero codes, zero
+    biases), so out = x + b2 of the chosen expert exactly."""
+    inp = make_layer_inputs(1, 2, 1, seed=11)
+    inp["x"] = bf16_bits_from_f32(np.ones((1, 2880), np.float32))
+    inp["Wr"] = np.zeros((2, 2880), np.float32)
+    inp["Wr"][0, :] = np.float32(1.0 / 2880.0)
+    inp["br"] = np.array([0.0, 0.9999975], np.float32)
+    for key in ("w13_codes", "w2_codes", "b13"):
+        inp[key][:] = 0
+    inp["b2"][0, :] = bf16_bits_from_f32(np.full(2880, 3.0, np.float32))
+    inp["b2"][1, :] = bf16_bits_from_f32(np.full(2880, -5.0, np.float32))
+    res = ob.block_forward(inp, 1, np.ones(2880), 1e-5)
+    wr0 = float(np.float32(1.0 / 2880.0)) * 2880.0   # expert 0's logit per unit input
+    assert wr0 / math.sqrt(1.0 + 1e-5) < 0.9999975 < wr0   # the two routes disagree
+    assert ob.normed_input_bits(inp["x"], np.ones(2880))[0, 0] == 0x3F80   # bf16(t) = 1.0
+    assert int(res["ids"][0, 0]) == 1
+    assert np.array_equal(res["out"], np.full((1, 2880), 1.0 - 5.0))
+
+
 ALL_CHECKS = [check_rmsnorm_python_loop, check_rmsnorm_constant_rows,
               check_rmsnorm_scale_invariance, check_bf16_rounding,
-              check_block_residual_and_zero_experts]
+              check_block_residual_and_zero_experts, check_block_routes_on_unrounded_norm]
