@@ -63,7 +63,10 @@
  * - `ws` is caller-owned device scratch, 256-byte aligned, of at least
  *   moe_workspace_size_op(op, T, E, k) bytes for the entry point's op
  *   (moe_workspace_size(T, E, k) is enough for every op). Its contents on
- *   entry do not matter.
+ *   entry do not matter. After a layer call (moe_forward, moe_forward_mx6,
+ *   moe_forward_block, on the stream) it starts with the routing: the
+ *   selected experts int32 [T*k] at offset 0, then their weights fp32 [T*k]
+ *   at offset T*k*4 rounded up to a multiple of 256.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -306,8 +309,8 @@ moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
 
 /* The MoE sublayer of a gpt-oss decoder layer with its neighbours: the
  * pre-MoE RMSNorm and the residual add.
- *   t   = bf16( x / sqrt(mean_h(x^2) + norm_eps) * norm_scale )   per token
- *   out = x + layer(t)          (layer = moe_forward on t, same kernels)
+ *   t   = x / sqrt(mean_h(x^2) + norm_eps) * norm_scale   per token (fp32)
+ *   out = x + layer(t): the router on t, the expert GEMMs on bf16(t)
  *   x          [T, 2880] bf16, the residual stream entering the sublayer
  *   norm_scale [2880] fp32 (16-byte aligned); norm_eps >= 0 (gpt-oss: 1e-5)
  *   out        [T, 2880] fp32 (overwritten)
@@ -315,8 +318,12 @@ moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
  * "gpt-oss-20b" page, "Structure" table (every layer runs RMSNorm_i_2 ->
  * MoE_i -> Add_i_ffn); techniques map, "normalization & residual" (RMSNorm,
  * Pre-LN); rms_norm_eps from the raw config.json tables. Readings: the norm
- * is computed in fp32 and its output rounded to bf16 (the layer's input
- * type); the residual is added in fp32. */
+ * is computed in fp32; the fp32 router takes it unrounded, as
+ * inv_rms * (x . (Wr[e] * norm_scale)); the expert GEMMs take it rounded to
+ * bf16 (their matrix-core input type); the residual is added in fp32. On the
+ * weight-streaming schedule with T <= 128 no norm kernel runs: the router
+ * forms each token's inverse RMS and the gate/up GEMM normalises x as it
+ * stages it. */
 moe_status_t moe_forward_block(const uint16_t* x, const float* norm_scale, float norm_eps,
                                const float* Wr, const float* br,
                                const moe_packed_weight_t* w13, const uint16_t* b13,

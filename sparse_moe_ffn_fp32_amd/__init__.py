@@ -27,7 +27,7 @@ from . import _native
 H = 2880
 I = 2880
 
-__all__ = ["MoeError", "PackedWeight", "PackedExperts", "workspace_size", "pack_weights",
+__all__ = ["MoeError", "PackedWeight", "PackedExperts", "workspace_size", "workspace_routing", "pack_weights",
            "pack_experts", "route", "permute", "expert_ffn", "gate_up", "down_accumulate",
            "combine", "forward", "forward_mx6", "encode_mx6", "gate_up_mx6", "forward_block",
            "rmsnorm", "forward_noalloc", "MX6_ROW_BYTES", "H", "I"]
@@ -151,6 +151,19 @@ def workspace_size(T: int, E: int, k: int, op: Optional[str] = None) -> int:
     if n == 0:
         raise ValueError(f"sizes out of range: T={T} E={E} k={k}")
     return n
+
+
+def workspace_routing(workspace: torch.Tensor, T: int, k: int):
+    """The routing a layer call leaves at the head of its workspace
+    (include/moe.h): expert ids int32 [T, k] and weights fp32 [T, k], as views."""
+    _dev(workspace, "workspace", _U8)
+    n = T * k
+    w_off = (n * 4 + 255) // 256 * 256
+    if workspace.numel() < w_off + n * 4:
+        raise ValueError("workspace too small for the routing of T tokens")
+    ids = workspace[: n * 4].view(torch.int32).view(T, k)
+    w = workspace[w_off: w_off + n * 4].view(torch.float32).view(T, k)
+    return ids, w
 
 
 def _workspace(T: int, E: int, k: int, device, ws: Optional[torch.Tensor], op: str) -> torch.Tensor:
@@ -372,8 +385,9 @@ def rmsnorm(x: torch.Tensor, scale: torch.Tensor, eps: float = 1e-5) -> torch.Te
 def forward_block(x, norm_scale, Wr, br, experts: PackedExperts, k: int = 4,
                   norm_eps: float = 1e-5, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out fp32 [T, 2880] = x + layer(bf16(RMSNorm(x))): the MoE sublayer of a
-    decoder layer with its pre-norm and residual add."""
+    """out fp32 [T, 2880] = x + layer(RMSNorm(x)): the MoE sublayer of a
+    decoder layer with its pre-norm and residual add (the router takes the
+    normed input in fp32, the expert GEMMs in bf16)."""
     T = x.shape[0]
     E = Wr.shape[0]
     _dev(x, "x", _BF16, (T, H))

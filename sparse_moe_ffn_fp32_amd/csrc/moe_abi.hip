@@ -24,7 +24,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t ids, w, counts, offsets, sorted, scratch, h, y, xrec, xnorm, hrec, total;
+  size_t ids, w, counts, offsets, sorted, scratch, h, y, xrec, xnorm, hrec, inv, total;
 };
 
 bool sizes_ok(int T, int E, int k) {
@@ -33,6 +33,15 @@ bool sizes_ok(int T, int E, int k) {
 }
 
 bool op_ok(int op) { return op >= MOE_OP_ROUTE && op <= MOE_OP_FORWARD_BLOCK; }
+
+// moe_forward_block without a norm kernel: the few-token router forms each
+// token's inverse RMS from its chunk sums of squares, and its finish launch
+// (without a permutation: the weight-streaming schedule) also writes the
+// normed rows for the expert GEMMs. Otherwise the norm kernel writes the rows
+// and the inverse RMS, which the router takes.
+bool block_norm_folded(int T, int E, int k) {
+  return moe::route_few_tokens(T, E) && !moe::ffn_uses_tiles(T * k, E);
+}
 
 // Carve-up of the workspace of entry point `op`: only what that call uses.
 // Regions an op does not use have size 0 (their offsets are then unused).
@@ -67,8 +76,12 @@ WsLayout layout(moe_op_t op, int T, int E, int k) {
   const bool mx6 = op == MOE_OP_FORWARD_MX6 && tiles;
   take(l.xrec, mx6 ? (size_t)T * moe::kRowRecBytes : 0);
   take(l.hrec, mx6 ? n * (size_t)moe::kRowRecBytes : 0);
-  // moe_forward_block: the normed bf16 input of the layer
-  take(l.xnorm, op == MOE_OP_FORWARD_BLOCK ? (size_t)T * moe::kH * 2 : 0);
+  // moe_forward_block: the normed bf16 input of the expert GEMMs, and the
+  // tokens' inverse RMS from the norm kernel (not when the router forms it,
+  // block_norm_folded)
+  const bool block = op == MOE_OP_FORWARD_BLOCK;
+  take(l.xnorm, block ? (size_t)T * moe::kH * 2 : 0);
+  take(l.inv, block && !block_norm_folded(T, E, k) ? (size_t)T * 4 : 0);
   l.total = off < kAlign ? kAlign : off;
   return l;
 }
@@ -208,7 +221,7 @@ moe_status_t moe_route(const uint16_t* x, const float* Wr, const float* br, int 
   float* scratch =
       reinterpret_cast<float*>(static_cast<char*>(ws) + layout(MOE_OP_ROUTE, T, E, k).scratch);
   return after_launch(moe::launch_route(x, Wr, br, T, E, k, topk_ids, topk_w, logits, scratch, nullptr,
-                                        nullptr, nullptr, s), s);
+                                        nullptr, nullptr, nullptr, s), s);
 }
 
 moe_status_t moe_pack_weights(const uint8_t* codes, const uint8_t* scales, int E, int N,
@@ -363,11 +376,21 @@ struct LayerWeights {
   const uint16_t* b2;
 };
 
-// The layer on x; with `resid` (bf16 [T, 2880]) the output is resid + layer.
+// The decoder block around the layer: the router's norm (scale, eps, the
+// inverse RMS or where the router writes the normed rows) and the expert
+// GEMMs' input, the normed bf16 rows `t`.
+struct BlockNorm {
+  moe::RouteNorm rn;
+  const uint16_t* t;
+};
+
+// The layer on x; with `resid` (bf16 [T, 2880]) the output is resid + layer;
+// with `blk` the layer of the decoder block on RMSNorm(x).
 // Arguments are validated by the caller; `l` is the caller's workspace layout.
 moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
                             const LayerWeights& lw, int T, int E, int k, float* out, char* base,
-                            const WsLayout& l, hipStream_t s, bool mx6, const uint16_t* resid) {
+                            const WsLayout& l, hipStream_t s, bool mx6, const uint16_t* resid,
+                            const BlockNorm* blk = nullptr) {
   int32_t* ids = reinterpret_cast<int32_t*>(base + l.ids);
   float* w = reinterpret_cast<float*>(base + l.w);
   int32_t* counts = reinterpret_cast<int32_t*>(base + l.counts);
@@ -381,8 +404,9 @@ moe_status_t forward_launch(const uint16_t* x, const float* Wr, const float* br,
   // The weight-streaming schedule needs no permutation arrays: its waves find
   // their slots in the routing ids.
   MOE_TRY(after_launch(moe::launch_route(x, Wr, br, T, E, k, ids, w, nullptr, scratch,
-                                         tiles ? counts : nullptr, offsets, sorted, s), s));
-  FfnArgs a13 = ffn_args(x, offsets, sorted, lw.w13, lw.b13, moe::kN13, E, k, 1);
+                                         tiles ? counts : nullptr, offsets, sorted,
+                                         blk ? &blk->rn : nullptr, s), s));
+  FfnArgs a13 = ffn_args(blk ? blk->t : x, offsets, sorted, lw.w13, lw.b13, moe::kN13, E, k, 1);
   a13.h_out = h;
   if (!tiles) {
     a13.ids = ids;
@@ -461,7 +485,7 @@ moe_status_t moe_rmsnorm(const uint16_t* x, const float* scale, float eps, int T
   if (!aligned(x, 16) || !aligned(t, 16) || !aligned(scale, 16)) return MOE_ERROR_MISALIGNED;
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(moe::launch_rmsnorm(x, scale, eps, T, t, s), s);
+  return after_launch(moe::launch_rmsnorm(x, scale, eps, T, t, nullptr, s), s);
 }
 
 moe_status_t moe_forward_block(const uint16_t* x, const float* norm_scale, float norm_eps,
@@ -480,10 +504,19 @@ moe_status_t moe_forward_block(const uint16_t* x, const float* norm_scale, float
   MOE_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   const WsLayout l = layout(MOE_OP_FORWARD_BLOCK, T, E, k);
-  uint16_t* t = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + l.xnorm);
-  MOE_TRY(after_launch(moe::launch_rmsnorm(x, norm_scale, norm_eps, T, t, s), s));
-  return forward_launch(t, Wr, br, LayerWeights{w13, b13, w2, b2}, T, E, k, out,
-                        static_cast<char*>(ws), l, s, false, x);
+  char* base = static_cast<char*>(ws);
+  uint16_t* t = reinterpret_cast<uint16_t*>(base + l.xnorm);
+  BlockNorm blk;
+  blk.rn = moe::RouteNorm{norm_scale, norm_eps, nullptr, false, t};
+  blk.t = t;
+  if (!block_norm_folded(T, E, k)) {
+    // the norm kernel writes the rows and the inverse RMS the router takes
+    float* inv = reinterpret_cast<float*>(base + l.inv);
+    MOE_TRY(after_launch(moe::launch_rmsnorm(x, norm_scale, norm_eps, T, t, inv, s), s));
+    blk.rn = moe::RouteNorm{norm_scale, norm_eps, inv, true, nullptr};
+  }
+  return forward_launch(x, Wr, br, LayerWeights{w13, b13, w2, b2}, T, E, k, out, base, l, s, false,
+                        x, &blk);
 }
 
 }  // extern "C"

@@ -95,6 +95,20 @@ __device__ __forceinline__ bf16x8 u4_as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// bf16(x * inv * scale) of 8 consecutive bf16 values (two per dword) and their
+// 8 scale values: the decoder block's RMSNorm applied to one 16-byte piece
+__device__ __forceinline__ uint4 norm_apply8(const uint4 d, float inv, const float4 s0,
+                                             const float4 s1) {
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+  const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = f32x2_to_bf16x2_bits(bf16_bits_to_f32(dw[q] & 0xFFFFu) * inv * s[2 * q],
+                                bf16_bits_to_f32(dw[q] >> 16) * inv * s[2 * q + 1]);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // gpt-oss gated unit for one (gate, up) pair, after the bias.
 __device__ __forceinline__ float swiglu_pair(float gate, float up) {
   constexpr float kNegAlphaLog2e = -kSwigluAlpha * 1.44269504088896341f;

@@ -42,11 +42,28 @@ struct FfnArgs {
   uint8_t* h6_out;
 };
 
+// The decoder block's RMSNorm folded into the router: the router's input is
+// t = x * inv * scale per token (inv = 1 / sqrt(mean(x^2) + eps)), computed as
+// inv * (x . (Wr[e] * scale)). `inv_ready`: inv [T] was written by the norm
+// kernel (required with many tokens). Otherwise (few tokens) the router forms
+// inv from x itself, and with `t_out` also writes the expert GEMMs' input
+// t_out = bf16(x * inv * scale) [T, 2880] (not with a permutation).
+struct RouteNorm {
+  const float* scale;   // [2880]
+  float eps;
+  const float* inv;     // [T]
+  bool inv_ready;
+  uint16_t* t_out;
+};
+
 // Router + top-k + softmax; with `counts` non-null the expert permutation is
-// built as well. `scratch` holds route_scratch_bytes(T, E) bytes.
+// built as well. `scratch` holds route_scratch_bytes(T, E) bytes. `norm`
+// (may be null): the decoder block's norm, above.
 hipError_t launch_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
                         int32_t* ids, float* w, float* logits, float* scratch,
-                        int32_t* counts, int32_t* offsets, int32_t* sorted_rows, hipStream_t s);
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
+                        const RouteNorm* norm, hipStream_t s);
+bool route_few_tokens(int T, int E);
 size_t route_scratch_bytes(int T, int E);
 
 // canonical MXFP4 codes/scales [E, N, ...] -> the packed order of the GEMMs
@@ -79,8 +96,9 @@ hipError_t launch_mx6_encode(const uint16_t* x, int rows, uint8_t* rec, hipStrea
 hipError_t launch_combine(const float* y, const float* w, int T, int k, const uint16_t* resid,
                           float* out, hipStream_t s);
 
-// t = bf16(x / sqrt(mean(x^2) + eps) * scale) per row of x [T, 2880] bf16
+// t = bf16(x / sqrt(mean(x^2) + eps) * scale) per row of x [T, 2880] bf16;
+// with `inv` non-null also each row's 1 / sqrt(mean(x^2) + eps) [T]
 hipError_t launch_rmsnorm(const uint16_t* x, const float* scale, float eps, int T, uint16_t* t,
-                          hipStream_t s);
+                          float* inv, hipStream_t s);
 
 }  // namespace moe

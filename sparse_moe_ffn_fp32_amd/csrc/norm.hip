@@ -47,32 +47,20 @@ __device__ __forceinline__ float norm_inv_rms(const uint4 (&d)[kNormPerLane], fl
   return 1.0f / sqrtf(t / (float)kH + eps);
 }
 
-// bf16(x * inv * scale) of 8 consecutive bf16 values (two per dword) and their
-// 8 scale values
-__device__ __forceinline__ uint4 norm_apply8(const uint4 d, float inv, const float4 s0,
-                                             const float4 s1) {
-  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-  const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    o[q] = f32x2_to_bf16x2_bits(bf16_bits_to_f32(dw[q] & 0xFFFFu) * inv * s[2 * q],
-                                bf16_bits_to_f32(dw[q] >> 16) * inv * s[2 * q + 1]);
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 // One wave per row, four rows per 256-thread block. The sum of squares is
 // reduced in a fixed order (per lane, then a butterfly), so results are
 // reproducible run to run.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x,
                                                       const float* __restrict__ scale, float eps,
-                                                      int T, uint16_t* __restrict__ t) {
+                                                      int T, uint16_t* __restrict__ t,
+                                                      float* __restrict__ inv_out) {
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= T) return;
   uint4 d[kNormPerLane];
   norm_load_raw(x + row * kH, lane, d);
   const float inv = norm_inv_rms(d, eps);
+  if (inv_out && lane == 0) inv_out[row] = inv;
   uint4* tr = reinterpret_cast<uint4*>(t + row * kH);
   const float4* sc = reinterpret_cast<const float4*>(scale);
 #pragma unroll
@@ -84,10 +72,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
 }
 
 hipError_t launch_rmsnorm(const uint16_t* x, const float* scale, float eps, int T, uint16_t* t,
-                          hipStream_t s) {
+                          float* inv, hipStream_t s) {
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, scale, eps,
-                     T, t);
+                     T, t, inv);
   return hipGetLastError();
 }
 

@@ -37,13 +37,15 @@ constexpr int kRouteMaxPairs = 4 * 1024;   // T * E of the few-token schedule (L
 static_assert(kRouteChunkSteps * 16 * kRouteChunks == kH, "chunks must tile K");
 
 static bool few_tokens(int T, int E) { return T <= kRouteSmallT && T * E <= kRouteMaxPairs; }
+bool route_few_tokens(int T, int E) { return few_tokens(T, E); }
 
 size_t route_split_bytes(int E);
 
 size_t route_scratch_bytes(int T, int E) {
-  // few tokens: K-chunk partial logits; many: the split weights, then the
+  // few tokens: K-chunk partial logits (and the decoder block's chunk sums of
+  // squares); many: the split weights, then the
   // per-32-token-group expert histograms
-  return few_tokens(T, E) ? (size_t)kRouteChunks * T * E * sizeof(float)
+  return few_tokens(T, E) ? (size_t)kRouteChunks * T * (E + 1) * sizeof(float)   // + sums of squares
                           : route_split_bytes(E) + (size_t)((T + 31) / 32) * E * sizeof(int32_t);
 }
 
@@ -78,25 +80,31 @@ template <int MT>
 struct RStage {
   uint4 xv;
   float4 w[MT][2];
+  float4 sc[2];   // NORM: the norm scale of the step's 8 K values
 };
 
 // Operand loader of one wave: tokens tok0 + (lane & 31), experts 32mt +
 // (lane & 31), K from k0 in steps of 16 (lane half hh takes 8 of them).
-template <int MT>
+// NORM: also the norm scale of the same K values (the router of the decoder
+// block takes Wr[e, h] * scale[h] as its weights, section "RMSNorm folded in"
+// of route_partial_kernel).
+template <int MT, bool NORM = false>
 struct RouteLoader {
   const uint16_t* xrow;
   bool tok_ok;
   const float* wrow[MT];
+  const float* srow;
   bool e_ok[MT];
 
-  __device__ __forceinline__ void init(const uint16_t* x, const float* Wr, int T, int E, int tok,
-                                       int k0, int lane) {
+  __device__ __forceinline__ void init(const uint16_t* x, const float* Wr, const float* scale, int T,
+                                       int E, int tok, int k0, int lane) {
     // padded tokens / experts read a clamped valid row: their results are
     // never used, and the loads stay unconditional
     const int n = lane & 31;
     const int hh = lane >> 5;
     tok_ok = tok < T;
     xrow = x + (size_t)min(tok, T - 1) * kH + k0 + 8 * hh;
+    srow = NORM ? scale + k0 + 8 * hh : nullptr;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int e = mt * 32 + n;
@@ -111,16 +119,37 @@ struct RouteLoader {
       st.w[mt][0] = *reinterpret_cast<const float4*>(wrow[mt] + 16 * s);
       st.w[mt][1] = *reinterpret_cast<const float4*>(wrow[mt] + 16 * s + 4);
     }
+    if (NORM) {
+      st.sc[0] = *reinterpret_cast<const float4*>(srow + 16 * s);
+      st.sc[1] = *reinterpret_cast<const float4*>(srow + 16 * s + 4);
+    }
   }
 };
 
-template <int MT>
-__device__ __forceinline__ void route_mma(const RStage<MT>& st, f32x16 (&acc)[MT]) {
+__device__ __forceinline__ float4 mul4(const float4 a, const float4 b) {
+  return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+
+// NORM: the weights are multiplied by the norm scale (rounded to fp32) before
+// the exact split, and `ss` accumulates the squares of the lane's 8 inputs.
+template <int MT, bool NORM = false>
+__device__ __forceinline__ void route_mma(const RStage<MT>& st, f32x16 (&acc)[MT], float& ss) {
   const bf16x8 xb = u4_as_bf16x8(st.xv);
+  if (NORM) {
+    const uint32_t dw[4] = {st.xv.x, st.xv.y, st.xv.z, st.xv.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x2 v = __builtin_bit_cast(bf16x2, dw[q]);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(v, v, ss, false);
+    }
+  }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     bf16x8 fh, fm, fl;
-    split_frag(st.w[mt][0], st.w[mt][1], fh, fm, fl);
+    if (NORM)
+      split_frag(mul4(st.w[mt][0], st.sc[0]), mul4(st.w[mt][1], st.sc[1]), fh, fm, fl);
+    else
+      split_frag(st.w[mt][0], st.w[mt][1], fh, fm, fl);
     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl, xb, acc[mt], 0, 0, 0);
     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fm, xb, acc[mt], 0, 0, 0);
     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh, xb, acc[mt], 0, 0, 0);
@@ -134,8 +163,9 @@ constexpr int route_depth() {
 
 // K loop over NSTEPS steps with a register prefetch ring, fully unrolled
 // (exact load counting).
-template <int MT, int NSTEPS>
-__device__ __forceinline__ void route_kloop(const RouteLoader<MT>& L, f32x16 (&acc)[MT]) {
+template <int MT, int NSTEPS, bool NORM = false>
+__device__ __forceinline__ void route_kloop(const RouteLoader<MT, NORM>& L, f32x16 (&acc)[MT],
+                                            float& ss) {
   static_assert(NSTEPS <= 16, "a longer unroll would spill");
   constexpr int D = route_depth<MT>() < NSTEPS ? route_depth<MT>() : NSTEPS;
   RStage<MT> st[D];
@@ -147,7 +177,7 @@ __device__ __forceinline__ void route_kloop(const RouteLoader<MT>& L, f32x16 (&a
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < NSTEPS; ++s) {
-    route_mma<MT>(st[s % D], acc);
+    route_mma<MT, NORM>(st[s % D], acc, ss);
     if (s + D < NSTEPS) L.load(st[s % D], s + D);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -253,8 +283,11 @@ size_t route_split_bytes(int E) {
   return (size_t)kRouteSteps * route_tiles_padded((E + 31) / 32) * 3 * 1024;
 }
 
-// MT = padded expert tiles of the layout; tiles past E are zero
-__global__ __launch_bounds__(256) void route_split_kernel(const float* __restrict__ Wr, int E,
+// MT = padded expert tiles of the layout; tiles past E are zero. With
+// `scale` (the decoder block's norm scale) the pieces are those of
+// Wr[e, h] * scale[h] rounded to fp32.
+__global__ __launch_bounds__(256) void route_split_kernel(const float* __restrict__ Wr,
+                                                          const float* __restrict__ scale, int E,
                                                           int MT, uint4* __restrict__ Wp) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= kRouteSteps * MT * 64) return;
@@ -267,6 +300,11 @@ __global__ __launch_bounds__(256) void route_split_kernel(const float* __restric
     const float* src = Wr + (size_t)e * kH + 16 * s + 8 * (lane >> 5);
     a = *reinterpret_cast<const float4*>(src);
     b = *reinterpret_cast<const float4*>(src + 4);
+    if (scale) {
+      const float* sc = scale + 16 * s + 8 * (lane >> 5);
+      a = mul4(a, *reinterpret_cast<const float4*>(sc));
+      b = mul4(b, *reinterpret_cast<const float4*>(sc + 4));
+    }
   }
   bf16x8 fh, fm, fl;
   split_frag(a, b, fh, fm, fl);
@@ -311,8 +349,8 @@ struct RTStage {
 template <int MT, int NTW, int KS>
 __global__ __launch_bounds__(KS * 64) void route_ksplit_kernel(
     const uint16_t* __restrict__ x, const uint4* __restrict__ Wp, const float* __restrict__ br,
-    int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wts,
-    float* __restrict__ logits, int32_t* __restrict__ block_hist) {
+    const float* __restrict__ inv, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ wts, float* __restrict__ logits, int32_t* __restrict__ block_hist) {
   using C = RouteTileCfg<MT, NTW, KS>;
   constexpr int D = C::kDepth;
   constexpr int LDR = C::kLdr;
@@ -390,6 +428,7 @@ __global__ __launch_bounds__(KS * 64) void route_ksplit_kernel(
     float v = red[e * LDR + t];
 #pragma unroll
     for (int w = 1; w < KS; ++w) v += red[(size_t)w * MT * 32 * LDR + e * LDR + t];
+    if (inv) v *= inv[min(tok0 + t, T - 1)];   // the decoder block's norm
     v += br[e];
     red[e * LDR + t] = v;
     if (logits && tok0 + t < T) logits[(size_t)(tok0 + t) * E + e] = v;
@@ -452,8 +491,8 @@ __device__ __forceinline__ int route_xs_off(int r, int p) { return r * 128 + ((p
 template <int MTW, int W, int NTW>
 __global__ __launch_bounds__(W * 64) void route_tile_kernel(
     const uint16_t* __restrict__ x, const uint4* __restrict__ Wp, const float* __restrict__ br,
-    int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wts,
-    float* __restrict__ logits, int32_t* __restrict__ block_hist) {
+    const float* __restrict__ inv, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ wts, float* __restrict__ logits, int32_t* __restrict__ block_hist) {
   using C = RouteWideCfg<MTW, W, NTW>;
   constexpr int D = C::kDepth;
   constexpr int TB = C::kTB;
@@ -579,7 +618,9 @@ __global__ __launch_bounds__(W * 64) void route_tile_kernel(
   // logits (+ bias) into LDS; 32x32 result layout: lane holds column n
   // (token), rows 8q + 4hh + j (experts)
 #pragma unroll
-  for (int tw = 0; tw < NTW; ++tw)
+  for (int tw = 0; tw < NTW; ++tw) {
+    // the decoder block's norm: the token's inverse RMS
+    const float iv = inv ? inv[min(tok0 + 32 * tw + n, T - 1)] : 1.f;
 #pragma unroll
     for (int m = 0; m < MTW; ++m)
 #pragma unroll
@@ -587,8 +628,10 @@ __global__ __launch_bounds__(W * 64) void route_tile_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 32 * (wave * MTW + m) + 8 * q + 4 * hh + j;
-          lg[e * LDR + 32 * tw + n] = acc[tw][m][4 * q + j] + (e < E ? br[e] : 0.f);
+          const float a = inv ? acc[tw][m][4 * q + j] * iv : acc[tw][m][4 * q + j];
+          lg[e * LDR + 32 * tw + n] = a + (e < E ? br[e] : 0.f);
         }
+  }
   __syncthreads();
   if (logits) {
     for (int i = tid; i < E * TB; i += W * 64) {
@@ -626,10 +669,19 @@ __global__ __launch_bounds__(W * 64) void route_tile_kernel(
 }
 
 // ---------------------------------------------------------------- few tokens
-template <int MT>
+// RMSNorm folded in (NORM, the decoder block, "gpt-oss-20b" page,
+// "Structure": RMSNorm_i_2 feeds MoE_i): the router's input is t = x * inv *
+// scale with inv = 1 / sqrt(mean(x^2) + eps) per token, so t . Wr[e] =
+// inv * (x . (Wr[e] * scale)). The chunk waves multiply x by the scaled
+// weights and also write their tokens' chunk sums of x^2 (ss, [chunk][T]);
+// the finish kernels add those in chunk order, form inv and scale the logits
+// by it. No kernel waits for a token's whole row before its products.
+template <int MT, bool NORM>
 __global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __restrict__ x,
-                                                           const float* __restrict__ Wr, int T,
-                                                           int E, float* __restrict__ partial) {
+                                                           const float* __restrict__ Wr,
+                                                           const float* __restrict__ scale, int T,
+                                                           int E, float* __restrict__ partial,
+                                                           float* __restrict__ ss_partial) {
   const int lane = threadIdx.x;
   const int n = lane & 31;
   const int hh = lane >> 5;
@@ -638,9 +690,11 @@ __global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __res
   f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
-  RouteLoader<MT> L;
-  L.init(x, Wr, T, E, tok, kc * kRouteChunkSteps * 16, lane);
-  route_kloop<MT, kRouteChunkSteps>(L, acc);
+  float ss = 0.f;
+  RouteLoader<MT, NORM> L;
+  L.init(x, Wr, scale, T, E, tok, kc * kRouteChunkSteps * 16, lane);
+  route_kloop<MT, kRouteChunkSteps, NORM>(L, acc, ss);
+  if (NORM) ss += __shfl_xor(ss, 32, 64);   // the two K halves of the token, lane order fixed
   if (tok < T) {
     float* prow = partial + ((size_t)kc * T + tok) * E;
 #pragma unroll
@@ -652,8 +706,32 @@ __global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __res
           const int e = mt * 32 + 8 * q + 4 * hh + j;
           if (e < E) prow[e] = acc[mt][4 * q + j];
         }
+    if (NORM && ss_partial && hh == 0) ss_partial[(size_t)kc * T + tok] = ss;
   }
 }
+
+// The norm's inverse RMS of token t from the chunk sums of squares, added in
+// chunk order.
+__device__ __forceinline__ float route_inv_rms(const float* __restrict__ ss_partial, int T, int t,
+                                               float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kRouteChunks; ++c) ss += ss_partial[(size_t)c * T + t];
+  return 1.0f / sqrtf(ss / (float)kH + eps);
+}
+
+// Norm arguments of the finish kernels: with `ss` the inverse RMS is formed
+// from the chunk sums; without `ss` but with `inv` it is read from there;
+// with neither the logits are not scaled.
+struct RouteFinishNorm {
+  const float* ss;
+  float eps;
+  const float* inv;
+  __device__ __forceinline__ float get(int T, int t) const {
+    if (ss) return route_inv_rms(ss, T, t, eps);
+    return inv ? inv[t] : 1.f;
+  }
+};
 
 // One 1024-thread block: logits = bias + sum of the chunk partials in chunk
 // order (one thread per (token, expert) pair, all partial loads in flight at
@@ -663,7 +741,8 @@ template <int PAIRS>
 __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(
     const float* __restrict__ partial, const float* __restrict__ br, int T, int E, int k,
     int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows) {
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
+    RouteFinishNorm nrm) {
   __shared__ PermuteSmem sm;
   __shared__ int lds_ids[kRouteSmallT * kMaxTopK];
   __shared__ float lg[kRouteMaxPairs + kMaxExperts];   // [E][T + 1]
@@ -690,7 +769,7 @@ __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(
     const int i = tid + j * kPermThreads;
     if (i < TE) {
       const int t = i / E, e = i - (i / E) * E;
-      const float v = acc[j] + bias[j];
+      const float v = (nrm.ss || nrm.inv) ? acc[j] * nrm.get(T, t) + bias[j] : acc[j] + bias[j];
       lg[e * ldt + t] = v;
       if (logits) logits[i] = v;
     }
@@ -728,14 +807,42 @@ __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(
   block_permute(lds_ids, T * k, E, counts, offsets, sorted_rows, sm);
 }
 
+// The decoder block's normed rows t = bf16(x * inv * scale) from the chunk
+// sums of squares, one wave per row (the norm kernel's arithmetic, with the
+// router's inverse RMS).
+__device__ __forceinline__ void route_write_normed_row(const uint16_t* __restrict__ x,
+                                                       const float* __restrict__ scale,
+                                                       const RouteFinishNorm& nrm, int T, int row,
+                                                       uint16_t* __restrict__ t) {
+  const int lane = threadIdx.x & 63;
+  const float inv = nrm.get(T, row);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * kH);
+  uint4* tr = reinterpret_cast<uint4*>(t + (size_t)row * kH);
+  const float4* sc = reinterpret_cast<const float4*>(scale);
+#pragma unroll
+  for (int j = 0; j < (kH / 8 + 63) / 64; ++j) {
+    const int i = lane + 64 * j;
+    if (i < kH / 8) tr[i] = norm_apply8(xr[i], inv, sc[2 * i], sc[2 * i + 1]);
+  }
+}
+
 // The same sums, top-k and softmax as route_finish_kernel without the
 // permutation, spread over blocks of 256 / E tokens each (one thread per
 // (token, expert) pair), so that the partial-logit loads of a decode batch
 // run on many CUs instead of one. Arithmetic in the same order: identical
-// expert choices and weights.
+// expert choices and weights. With `t_out` (the decoder block), blocks from
+// `nfin` on write the normed rows instead, four per block, so the block needs
+// no separate norm launch.
 __global__ __launch_bounds__(256) void route_finish_tiles_kernel(
     const float* __restrict__ partial, const float* __restrict__ br, int T, int E, int k, int tb,
-    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits) {
+    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits,
+    RouteFinishNorm nrm, int nfin, const uint16_t* __restrict__ x, const float* __restrict__ nscale,
+    uint16_t* __restrict__ t_out) {
+  if ((int)blockIdx.x >= nfin) {
+    const int row = ((int)blockIdx.x - nfin) * 4 + (int)(threadIdx.x >> 6);
+    if (row < T) route_write_normed_row(x, nscale, nrm, T, row, t_out);
+    return;
+  }
   __shared__ float lg[256];
   __shared__ float sel_v[256];
   __shared__ int sel_e[256];
@@ -750,6 +857,7 @@ __global__ __launch_bounds__(256) void route_finish_tiles_kernel(
     float acc = 0.f;
 #pragma unroll
     for (int c = 0; c < kRouteChunks; ++c) acc += partial[(size_t)c * TE + i];
+    if (nrm.ss || nrm.inv) acc *= nrm.get(T, t0 + tid / E);
     v = acc + br[tid % E];
     lg[tid] = v;
     if (logits) logits[i] = v;
@@ -778,11 +886,11 @@ __global__ __launch_bounds__(256) void route_finish_tiles_kernel(
 
 static void launch_finish(const float* scratch, const float* br, int T, int E, int k, int32_t* ids,
                           float* w, float* logits, int32_t* counts, int32_t* offsets,
-                          int32_t* sorted_rows, hipStream_t s) {
+                          int32_t* sorted_rows, const RouteFinishNorm& fn, hipStream_t s) {
   const int pairs = (T * E + kPermThreads - 1) / kPermThreads;
 #define MOE_FINISH(P)                                                                             \
   hipLaunchKernelGGL((route_finish_kernel<P>), dim3(1), dim3(kPermThreads), 0, s, scratch,          \
-                     br, T, E, k, ids, w, logits, counts, offsets, sorted_rows)
+                     br, T, E, k, ids, w, logits, counts, offsets, sorted_rows, fn)
   if (pairs <= 1) MOE_FINISH(1);
   else if (pairs <= 2) MOE_FINISH(2);
   else MOE_FINISH(4);
@@ -794,30 +902,46 @@ template <int MT>
 static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const float* br, int T, int E,
                                   int k, int32_t* ids, float* w, float* logits,
                                   float* scratch, int32_t* counts, int32_t* offsets,
-                                  int32_t* sorted_rows, hipStream_t s) {
+                                  int32_t* sorted_rows, const RouteNorm* norm, hipStream_t s) {
   if (few_tokens(T, E)) {
     const dim3 grid((T + 31) / 32, kRouteChunks);
-    hipLaunchKernelGGL((route_partial_kernel<MT>), grid, dim3(64), 0, s, x, Wr, T, E, scratch);
+    // the chunk sums of squares follow the partial logits
+    float* ss = norm && !norm->inv_ready ? scratch + (size_t)kRouteChunks * T * E : nullptr;
+    if (norm)
+      hipLaunchKernelGGL((route_partial_kernel<MT, true>), grid, dim3(64), 0, s, x, Wr, norm->scale, T, E,
+                         scratch, ss);
+    else
+      hipLaunchKernelGGL((route_partial_kernel<MT, false>), grid, dim3(64), 0, s, x, Wr, nullptr, T, E,
+                         scratch, nullptr);
+    const RouteFinishNorm fn{ss, norm ? norm->eps : 0.f, norm ? norm->inv : nullptr};
+    uint16_t* t_out = ss ? norm->t_out : nullptr;   // the normed rows, from the router's sums
     if (counts) {
-      launch_finish(scratch, br, T, E, k, ids, w, logits, counts, offsets, sorted_rows, s);
+      if (t_out) return hipErrorInvalidValue;
+      launch_finish(scratch, br, T, E, k, ids, w, logits, counts, offsets, sorted_rows, fn, s);
     } else {
       const int tb = 256 / E;   // tokens per block; E <= 256
-      hipLaunchKernelGGL(route_finish_tiles_kernel, dim3((T + tb - 1) / tb), dim3(256), 0, s, scratch,
-                         br, T, E, k, tb, ids, w, logits);
+      const int nfin = (T + tb - 1) / tb;
+      const int nwrite = t_out ? (T + 3) / 4 : 0;
+      hipLaunchKernelGGL(route_finish_tiles_kernel, dim3(nfin + nwrite), dim3(256), 0, s, scratch, br,
+                         T, E, k, tb, ids, w, logits, fn, nfin, x, norm ? norm->scale : nullptr, t_out);
     }
     return hipGetLastError();
   }
+  // many tokens: the norm's inverse RMS comes from the norm kernel
+  if (norm && (!norm->inv_ready || !norm->inv)) return hipErrorInvalidValue;
+  const float* nscale = norm ? norm->scale : nullptr;
+  const float* ninv = norm ? norm->inv : nullptr;
   // split weights first (16-byte aligned: a multiple of 1 KiB), then the histograms
   constexpr int MTP = route_tiles_padded(MT);
   uint4* wp = reinterpret_cast<uint4*>(scratch);
   int32_t* hist = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(scratch) + route_split_bytes(E));
   hipLaunchKernelGGL(route_split_kernel, dim3((kRouteSteps * MTP * 64 + 255) / 256), dim3(256), 0, s,
-                     Wr, E, MTP, wp);
+                     Wr, nscale, E, MTP, wp);
   int32_t* bh = counts ? hist : nullptr;
   if constexpr (MT <= 2) {
     // few expert tiles: waves split K (little work per wave and step)
     hipLaunchKernelGGL((route_ksplit_kernel<MT, 1, 12>), dim3((T + 31) / 32), dim3(12 * 64), 0, s, x,
-                       wp, br, T, E, k, ids, w, logits, bh);
+                       wp, br, ninv, T, E, k, ids, w, logits, bh);
   } else {
     // a wave per one or two expert tiles; two token tiles per wave (half the
     // weight traffic per token) once 64-token blocks alone fill the chip
@@ -825,10 +949,10 @@ static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const floa
     constexpr int WV = MTP / MTW;
     if ((T + 63) / 64 >= kRouteTwoTileBlocks)
       hipLaunchKernelGGL((route_tile_kernel<MTW, WV, 2>), dim3((T + 63) / 64), dim3(WV * 64), 0, s, x,
-                         wp, br, T, E, k, ids, w, logits, bh);
+                         wp, br, ninv, T, E, k, ids, w, logits, bh);
     else
       hipLaunchKernelGGL((route_tile_kernel<MTW, WV, 1>), dim3((T + 31) / 32), dim3(WV * 64), 0, s, x,
-                         wp, br, T, E, k, ids, w, logits, bh);
+                         wp, br, ninv, T, E, k, ids, w, logits, bh);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !counts) return err;
@@ -838,18 +962,24 @@ static hipError_t launch_route_mt(const uint16_t* x, const float* Wr, const floa
 
 hipError_t launch_route(const uint16_t* x, const float* Wr, const float* br, int T, int E, int k,
                         int32_t* ids, float* w, float* logits, float* scratch,
-                        int32_t* counts, int32_t* offsets, int32_t* sorted_rows, hipStream_t s) {
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
+                        const RouteNorm* norm, hipStream_t s) {
+#define MOE_ROUTE(M)                                                                                \
+  case M:                                                                                           \
+    return launch_route_mt<M>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets,         \
+                              sorted_rows, norm, s)
   switch ((E + 31) / 32) {
-    case 1: return launch_route_mt<1>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
-    case 2: return launch_route_mt<2>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
-    case 3: return launch_route_mt<3>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
-    case 4: return launch_route_mt<4>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
-    case 5: return launch_route_mt<5>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
-    case 6: return launch_route_mt<6>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
-    case 7: return launch_route_mt<7>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
-    case 8: return launch_route_mt<8>(x, Wr, br, T, E, k, ids, w, logits, scratch, counts, offsets, sorted_rows, s);
+    MOE_ROUTE(1);
+    MOE_ROUTE(2);
+    MOE_ROUTE(3);
+    MOE_ROUTE(4);
+    MOE_ROUTE(5);
+    MOE_ROUTE(6);
+    MOE_ROUTE(7);
+    MOE_ROUTE(8);
     default: return hipErrorInvalidValue;
   }
+#undef MOE_ROUTE
 }
 
 }  // namespace moe

@@ -82,6 +82,9 @@ def test_workspace_size_per_op(L):
     assert ws("forward_mx6", T, E, k) >= fwd + (T + n) * 5888
     assert ws("forward_block", T, E, k) >= fwd + T * 2880 * 2
     assert ws("forward_block", T, E, k) < ws("forward_mx6", T, E, k)
+    # decode sizes: the router forms the inverse RMS itself (no buffer for
+    # it), only the normed rows are added
+    assert ws("forward_block", 64, 32, 4) == ws("forward", 64, 32, 4) + 64 * 2880 * 2
     # decode sizes: no records (weight-streaming schedule)
     assert ws("forward_mx6", 64, 32, 4) == ws("forward", 64, 32, 4)
     # the all-ops size is the largest

@@ -70,13 +70,16 @@ def test_forward_graph_replays(T, E, k, path):
         got = out.clone()
         assert torch.isfinite(got).all(), f"replay {r}: non-finite"
         assert torch.equal(got, eager), f"replay {r} differs"
-    # the replayed output against the oracle (the block: out - x against the
-    # oracle's block on its own normed input)
+    # the replayed output against the oracle (the block: the routing the
+    # replay left in the workspace against the oracle's routing of the normed
+    # input, and out - x against the oracle's block)
     torch.cuda.synchronize()
     if path == "block":
-        t = moe.rmsnorm(d["x"], g)
-        ids, w = moe.route(t, d["Wr"], d["br"], k=k)
-        ref = ob.block_forward(inp, k, np.full(2880, 1.5, dtype=np.float32), ids_override=ids.cpu().numpy())
+        ids, w = moe.workspace_routing(ws, T, k)
+        g64 = np.full(2880, 1.5, dtype=np.float32)
+        check_routing(ids.cpu().numpy(), w.cpu().numpy(),
+                      oracle.router_logits_f64(ob.rmsnorm(inp["x"], g64), inp["Wr"], inp["br"]), k)
+        ref = ob.block_forward(inp, k, g64, ids_override=ids.cpu().numpy())
         x64 = oracle.bf16_to_f64(inp["x"])
         assert_out_close(got.cpu().numpy() - x64, ref["out"] - x64, "graph replay, block")
     else:
