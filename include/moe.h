@@ -320,10 +320,10 @@ moe_status_t moe_gate_up_mx6(const uint8_t* x_records, const int32_t* offsets,
  * Pre-LN); rms_norm_eps from the raw config.json tables. Readings: the norm
  * is computed in fp32; the fp32 router takes it unrounded, as
  * inv_rms * (x . (Wr[e] * norm_scale)); the expert GEMMs take it rounded to
- * bf16 (their matrix-core input type); the residual is added in fp32. On the
- * weight-streaming schedule with T <= 128 no norm kernel runs: the router
- * forms each token's inverse RMS and the gate/up GEMM normalises x as it
- * stages it. */
+ * bf16 (their matrix-core input type); the residual is added in fp32. With
+ * few tokens (T <= 128, T*E <= 4096) on the weight-streaming schedule no
+ * norm kernel runs: the router forms each token's inverse RMS from its own
+ * sums of squares and its finish launch writes the normed rows. */
 moe_status_t moe_forward_block(const uint16_t* x, const float* norm_scale, float norm_eps,
                                const float* Wr, const float* br,
                                const moe_packed_weight_t* w13, const uint16_t* b13,
