@@ -212,6 +212,29 @@ def test_expert_ffn_and_combine(T, E, k):
     assert_out_close(np_(out), ref["out"], "combine")
 
 
+def test_expert_ffn_every_tile_size():
+    """Expert row counts on both sides of every 32-token boundary of the tiled
+    GEMMs (an expert's last tile loads and multiplies 1, 2, 3 or 4 token
+    tiles; 128-row tiles before it), routing fixed by hand (k = 1, E = 16,
+    tokens assigned to experts in a shuffled order so the gather is not the
+    identity): every slot's y against the oracle."""
+    counts = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 159, 255, 257]
+    E, k = len(counts), 1
+    T = sum(counts)
+    say(f"expert_ffn every tile size: T={T} E={E} counts {counts}")
+    inp = make_layer_inputs(T, E, k, seed=6100)
+    ids = np.repeat(np.arange(E), counts)[np.random.default_rng(6101).permutation(T)].reshape(T, 1)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = np.argsort(ids[:, 0], kind="stable").astype(np.int32)   # slot t*k + j = t
+    d = to_device(inp)
+    y = moe.expert_ffn(d["x"], torch.from_numpy(offsets).cuda(), torch.from_numpy(rows).cuda(),
+                       *weights_args(d), k=k)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp, k, ids_override=ids, keep_y=True)
+    m = assert_out_close(np_(y).reshape(T * k, -1), ref["y"].reshape(T * k, -1), "y, every tile size")
+    say(f"  metrics {m}")
+
+
 @pytest.mark.parametrize("T,E,k", SMALL_CASES)
 def test_forward_small(T, E, k):
     say(f"forward T={T} E={E} k={k}")
