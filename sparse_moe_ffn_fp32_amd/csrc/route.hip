@@ -23,6 +23,10 @@
 //    and add their partial tiles in wave order through LDS, then select the
 //    top k and count the routed slots per expert of each 32-token group for
 //    the parallel permutation.
+// The decoder block's pre-MoE RMSNorm folds into either schedule (RouteNorm):
+// the weights are scaled by the norm scale and each token's logits by its
+// inverse RMS, which the few-token schedule forms from its own sums of
+// squares.
 #include "moe_block_permute.h"
 #include "moe_device.h"
 #include "moe_launch.h"
@@ -86,8 +90,8 @@ struct RStage {
 // Operand loader of one wave: tokens tok0 + (lane & 31), experts 32mt +
 // (lane & 31), K from k0 in steps of 16 (lane half hh takes 8 of them).
 // NORM: also the norm scale of the same K values (the router of the decoder
-// block takes Wr[e, h] * scale[h] as its weights, section "RMSNorm folded in"
-// of route_partial_kernel).
+// block takes Wr[e, h] * scale[h] as its weights; the comment above
+// route_partial_kernel gives the algebra).
 template <int MT, bool NORM = false>
 struct RouteLoader {
   const uint16_t* xrow;
