@@ -848,10 +848,13 @@ __host__ __device__ constexpr int tl_wait_mid(int s) {
 // 2 for a tile of at most 64 tokens); this wave computes NTA of them from
 // tile nt0 on, for weight group G (local group gloc of the column block).
 template <int EPI, int NTL, int NTA, bool W_OK>
-__device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const int* slot_of,
-                                         int* xrow_of, const uint16_t* bias_s, int e, int G,
+__device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, int* slot_of,
+                                         int* xrow_of, uint16_t* bias_s, int e, int G,
                                          int gloc, int nt0, int rb, int re) {
   constexpr bool w_ok = W_OK;
+  // the down projection reads rows rb + t of h (sorted order): its copies need
+  // no lookup, and its slot and bias rows are loaded behind them
+  constexpr bool kDirect = EPI != EPI_SWIGLU;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -871,7 +874,8 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
   for (int j = 0; j < kTlXLoads; ++j) {
     const int t = 4 * (kTlXLoads * wave + j) + (lane >> 4);
     const int kp = (q_lds ^ ((4 * j + (lane >> 4)) & 15)) * 8;   // t & 15 = (4j + (lane >> 4)) & 15
-    xsrc[j] = a.act + (size_t)xrow_of[t] * kH + kp;
+    const int xrow = kDirect ? rb + (rb + t < re ? t : 0) : xrow_of[t];
+    xsrc[j] = a.act + (size_t)xrow * kH + kp;
   }
   auto load_x_one = [&](uint8_t* dst, int s, int j) __attribute__((always_inline)) {
     if (4 * (kTlXLoads * wave + j) >= kLoadRows) return;   // wave-uniform
@@ -987,20 +991,34 @@ __device__ __forceinline__ void tile_run(const FfnArgs& a, uint8_t* xs, const in
     for (int j = 0; j < kTlXLoads; ++j) load_x_one(stage(s), s, j);
   // D[weight row][token]: lane holds token column c of tile nt and weight
   // rows 32mt + 8q + 4h + j (j = 0..3) of the wave's group. The accumulators
-  // start from the rows' biases (while the first loads are in flight), so the
-  // epilogue has no bias to add.
+  // start from the rows' biases, so the epilogue has no bias to add.
+  auto init_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float b = w_ok ? bf16_bits_to_f32(bias_s[gloc * 64 + 32 * mt + 8 * q + 4 * h + j]) : 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const float b = w_ok ? bf16_bits_to_f32(bias_s[gloc * 64 + 32 * mt + 8 * q + 4 * h + j]) : 0.f;
 #pragma unroll
-        for (int nt = 0; nt < NTA; ++nt) acc[mt][nt][4 * q + j] = b;
-      }
+          for (int nt = 0; nt < NTA; ++nt) acc[mt][nt][4 * q + j] = b;
+        }
+  };
+  if constexpr (kDirect) {
+    // the tile's slots (for the y rows) and biases, behind its first copies;
+    // every thread's LDS stores are done before the barrier below
+    const int tid0 = threadIdx.x;
+    if (tid0 < kTlBT) slot_of[tid0] = rb + tid0 < re ? a.sorted_rows[rb + tid0] : -1;
+    const int row = (G / kTlWaves) * kTlRows + tid0;   // the column block's row tid0
+    bias_s[tid0] = row < a.N ? a.bias[(size_t)e * a.N + row] : 0;
+    // the barrier below does not wait for LDS stores: this thread's are done
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  } else {
+    init_acc();   // while the first loads are in flight
+  }
   wait_for(2 * kTlXLoads);   // X(0) and both weight steps
   __builtin_amdgcn_s_barrier();
+  if constexpr (kDirect) init_acc();
   read_x(stage(0), 0, xf);
   // every step is its own straight-line code (compile-time step index): the
   // waits, ring slots and stage offsets are constants, and the compiler's own
@@ -1119,11 +1137,12 @@ __device__ __forceinline__ int tl_wave_role(int gl, int ntl, int wave, int& gloc
 // The instance of tile_run for a wave's role (tl_wave_role) in a tile of NTL
 // loaded 32-token tiles; with one token tile roles 0 and 1 coincide.
 template <int EPI, int NTL>
-__device__ __forceinline__ void tile_roles(int role, const FfnArgs& a, uint8_t* xs, const int* slot_of,
-                                           int* xrow_of, const uint16_t* bias_s, int e, int G,
+__device__ __forceinline__ void tile_roles(int role, const FfnArgs& a, uint8_t* xs, int* slot_of,
+                                           int* xrow_of, uint16_t* bias_s, int e, int G,
                                            int gloc, int nt0, int rb, int re) {
   if (role == 2) {
-    tile_run<EPI, NTL, 1, false>(a, xs, slot_of, xrow_of, bias_s, e, 0, 0, 0, rb, re);
+    // G only locates the column block here (the wave loads group 0's weights)
+    tile_run<EPI, NTL, 1, false>(a, xs, slot_of, xrow_of, bias_s, e, G, 0, 0, rb, re);
   } else if (NTL == 1 || role == 1) {
     tile_run<EPI, NTL, 1, true>(a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re);
   } else {
@@ -1156,18 +1175,21 @@ __global__ __launch_bounds__(kTlThreads) __attribute__((amdgpu_waves_per_eu(2)))
   gloc = __builtin_amdgcn_readfirstlane(gloc);
   nt0 = __builtin_amdgcn_readfirstlane(nt0);
   const int G = wx * kTlWaves + gloc;
-  if (tid < kTlBT) slot_of[tid] = tid < nvalid ? a.sorted_rows[rb + tid] : -1;
-  {
-    const int row = wx * kTlRows + tid;
-    bias_s[tid] = row < a.N ? a.bias[(size_t)e * a.N + row] : 0;
+  if constexpr (EPI == EPI_SWIGLU) {
+    // gate/up: the activation rows come through the slots
+    if (tid < kTlBT) slot_of[tid] = tid < nvalid ? a.sorted_rows[rb + tid] : -1;
+    {
+      const int row = wx * kTlRows + tid;
+      bias_s[tid] = row < a.N ? a.bias[(size_t)e * a.N + row] : 0;
+    }
+    __syncthreads();
+    // activation row of each token row of the tile (padded rows: the first)
+    if (tid < kTlBT) {
+      const int tv = tid < nvalid ? tid : 0;
+      xrow_of[tid] = a.gather ? slot_of[tv] / a.k : rb + tv;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  // activation row of each token row of the tile (padded rows: the first)
-  if (tid < kTlBT) {
-    const int tv = tid < nvalid ? tid : 0;
-    xrow_of[tid] = a.gather ? slot_of[tv] / a.k : rb + tv;
-  }
-  __syncthreads();
   switch (ntl) {
     case 4: tile_roles<EPI, 4>(role, a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re); break;
     case 3: tile_roles<EPI, 3>(role, a, xs, slot_of, xrow_of, bias_s, e, G, gloc, nt0, rb, re); break;
@@ -1208,6 +1230,8 @@ hipError_t launch_ffn(const FfnArgs& a, Epilogue epi, int n_rows, hipStream_t s)
       }
       return hipGetLastError();
     }
+    // the tiled down instances take h rows in sorted order (rb + t)
+    if (epi != EPI_SWIGLU && a.gather) return hipErrorInvalidValue;
     const int tl_tiles = (n_rows + kTlBT - 1) / kTlBT + min(a.E, n_rows);
     const dim3 tl_grid(((groups + kTlWaves - 1) / kTlWaves) * tl_tiles);
     switch (epi) {
