@@ -82,12 +82,13 @@ def router_logits_of_block(inp, g):
 
 
 # Norm folded into the router and the weight-streaming gate/up (T <= 128,
-# T*E <= 4096): (1, 4, 1), (16, 32, 4), (100, 40, 4), (8, 256, 4) (eight expert
-# tiles per router wave, one token per finish block); the norm kernel with the
+# T*E <= 4096): (1, 4, 1), (16, 32, 4), (100, 40, 4), (128, 32, 4) (the
+# largest: T*E = 4096), (8, 256, 4) (eight expert tiles per router wave, one
+# token per finish block); the norm kernel with the
 # weight-streaming GEMMs on its output (many-token router, K-split and
 # expert-tiled): (200, 32, 4), (160, 80, 4); with the tiled GEMMs: (128, 8, 8)
 # (few-token router), (130, 2, 2), (256, 8, 4), (300, 4, 1).
-BLOCK_CASES = [(1, 4, 1), (16, 32, 4), (100, 40, 4), (8, 256, 4), (200, 32, 4), (160, 80, 4), (128, 8, 8),
+BLOCK_CASES = [(1, 4, 1), (16, 32, 4), (100, 40, 4), (128, 32, 4), (8, 256, 4), (200, 32, 4), (160, 80, 4), (128, 8, 8),
                (130, 2, 2), (256, 8, 4), (300, 4, 1)]
 
 
